@@ -1,0 +1,16 @@
+"""The oracle: a plain, slow, obviously correct fp64 CPU attention (forward, backward,
+block-sparse pattern).
+
+TEST INFRASTRUCTURE ONLY. It exists to check the HIP library. Only ``tests/``,
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import it.
+It imports nothing from the product package and shares no code with it; the only
+module both sides use is ``workloads`` (seeded random inputs, no attention math).
+"""
+from .attention import (KeySets, attention_backward, attention_forward, backward_rows_dq,
+                        forward_row, row_probabilities, row_scores)
+from .block_rule import allowed_blocks, block_lists, key_mask_from_lists
+
+__all__ = [
+    "KeySets", "attention_forward", "attention_backward", "backward_rows_dq", "forward_row",
+    "row_probabilities", "row_scores", "allowed_blocks", "block_lists", "key_mask_from_lists",
+]
