@@ -1,0 +1,19 @@
+"""MI355X-native tiled exact attention (dense, causal, block-sparse forward; recomputation
+backward), as a thin Python binding over the C ABI of libfa.so.
+
+Every step of the computation runs in the library's gfx950 kernels; this module only
+marshals torch tensors (device memory and the current stream) into the C calls. There is
+no CPU or eager fallback: a missing library raises at import, a bad argument raises
+``FaError`` with the library's status and detail.
+
+    o, lse = fwd(q, k, v, causal=True)                   # q, k, v: bf16 [B, H, N, d] views
+    o, lse = sparse_fwd(q, k, v, offsets, indices)       # Flash-MSA block lists (CSR, int32)
+    dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)
+    offsets, indices = make_block_lists(n_blocks, window=8, stride=16)
+"""
+from ._lib import EXPORTS, FA_STATUS, LIB_PATH, FaError, Strides, lib
+from .api import (bwd, bwd_workspace_bytes, check_block_lists, fwd, make_block_lists, sparse_fwd,
+                  status_str)
+
+__all__ = ["fwd", "sparse_fwd", "bwd", "bwd_workspace_bytes", "make_block_lists", "check_block_lists",
+           "status_str", "FaError", "Strides", "lib", "LIB_PATH", "EXPORTS", "FA_STATUS"]

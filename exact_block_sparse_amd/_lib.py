@@ -1,0 +1,67 @@
+"""ctypes loader for libfa.so (built in-tree by exact_block_sparse_amd.build).
+
+There is no fallback: if the library is missing or fails to load, importing the package
+raises, naming the build command.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_STATUS = {
+    0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 4: "FA_ERR_LAYOUT",
+    5: "FA_ERR_LIST", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP", 8: "FA_ERR_ARG", 9: "FA_ERR_CAPACITY",
+}
+EXPORTS = ("fa_fwd", "fa_sparse_fwd", "fa_bwd_workspace_bytes", "fa_bwd", "fa_make_block_lists",
+           "fa_check_block_lists", "fa_status_str", "fa_last_error")
+
+
+class Strides(ctypes.Structure):
+    """fa_strides: element strides (b, h, n) of a logical [B, H, N, d] tensor."""
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("n", ctypes.c_int64)]
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, detail: str, call: str):
+        self.status = status
+        self.name = FA_STATUS.get(status, f"status {status}")
+        super().__init__(f"{call}: {self.name}: {detail}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m exact_block_sparse_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    S = Strides
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, S, S, S, S, i32, f32, vp]
+    lib.fa_fwd.restype = i32
+    lib.fa_sparse_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, S, S, S, S,
+                                  i64, vp, vp, i64, i32, f32, vp]
+    lib.fa_sparse_fwd.restype = i32
+    lib.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                           S, S, S, S, S, S, S, S, i32, f32, vp, ctypes.c_size_t, vp]
+    lib.fa_bwd.restype = i32
+    lib.fa_make_block_lists.argtypes = [i64, ctypes.c_int32, ctypes.c_int32, i32, i32, pi32, pi32, i64,
+                                        ctypes.POINTER(ctypes.c_int64)]
+    lib.fa_make_block_lists.restype = i32
+    lib.fa_check_block_lists.argtypes = [pi32, pi32, i64, i64, i32]
+    lib.fa_check_block_lists.restype = i32
+    lib.fa_status_str.argtypes = [i32]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def check(status: int, call: str) -> None:
+    if status != 0:
+        raise FaError(status, lib.fa_last_error().decode(errors="replace"), call)

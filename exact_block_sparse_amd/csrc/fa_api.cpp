@@ -1,0 +1,253 @@
+// C ABI of libfa.so: host-side argument validation, block-list utilities and launches.
+// Declarations, argument meanings and the passages they follow are in include/fa.h.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "fa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return FA_OK;
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;   // B, H, N each stay well inside int32
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_sizes(int64_t B, int64_t H, int64_t N, int64_t d) {
+    if (B < 0 || H < 0 || N < 0)
+        return fail(FA_ERR_SHAPE, "negative size B=%lld H=%lld N=%lld", (long long)B, (long long)H, (long long)N);
+    if (B > kMaxDim || H > kMaxDim || N > kMaxDim || B * H > kMaxDim)
+        return fail(FA_ERR_SHAPE, "size too large B=%lld H=%lld N=%lld", (long long)B, (long long)H, (long long)N);
+    if (d != 64 && d != 128) return fail(FA_ERR_HEADDIM, "head dimension %lld not supported (64 or 128)", (long long)d);
+    return FA_OK;
+}
+
+int check_tensor(const char* name, const void* p, const fa_strides& s) {
+    if (!p) return fail(FA_ERR_NULL, "%s is NULL", name);
+    if (!aligned16(p)) return fail(FA_ERR_LAYOUT, "%s is not 16-byte aligned", name);
+    if ((s.b % 8) || (s.h % 8) || (s.n % 8))
+        return fail(FA_ERR_LAYOUT, "%s strides (%lld, %lld, %lld) are not multiples of 8 elements", name,
+                    (long long)s.b, (long long)s.h, (long long)s.n);
+    if (s.b < 0 || s.h < 0 || s.n < 0) return fail(FA_ERR_LAYOUT, "%s has a negative stride", name);
+    return FA_OK;
+}
+
+int check_device() {
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        return fail(FA_ERR_HIP, "no HIP device available (%s)", hipGetErrorString(e));
+    }
+    return FA_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+fa::View view(const void* p, const fa_strides& s) { return fa::View{p, s.b, s.h, s.n}; }
+
+int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+               int64_t N, int64_t d, fa_strides sq, fa_strides sk, fa_strides sv, fa_strides so, int causal,
+               float scale, const int32_t* kv_offsets, const int32_t* kv_indices, int64_t nnz,
+               void* stream) {
+    int st = check_sizes(B, H, N, d);
+    if (st) return st;
+    if (!std::isfinite(scale)) return fail(FA_ERR_ARG, "scale is not finite");
+    if (B == 0 || H == 0 || N == 0) return ok();
+    if ((st = check_tensor("q", q, sq)) || (st = check_tensor("k", k, sk)) || (st = check_tensor("v", v, sv)) ||
+        (st = check_tensor("o", o, so)))
+        return st;
+    if (!lse) return fail(FA_ERR_NULL, "lse is NULL");
+    if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(FA_ERR_LAYOUT, "lse is not 4-byte aligned");
+    if ((st = check_device())) return st;
+    fa::FwdArgs a;
+    a.q = view(q, sq);
+    a.k = view(k, sk);
+    a.v = view(v, sv);
+    a.o = o;
+    a.osb = so.b; a.osh = so.h; a.osn = so.n;
+    a.lse = lse;
+    a.B = (int)B; a.H = (int)H; a.N = (int)N; a.d = (int)d;
+    a.causal = causal != 0;
+    a.scale = scale;
+    a.kv_offsets = kv_offsets;
+    a.kv_indices = kv_indices;
+    a.nnz = nnz;
+    return launched(fa::launch_fwd(a, static_cast<hipStream_t>(stream)), "forward");
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+           int64_t d, fa_strides sq, fa_strides sk, fa_strides sv, fa_strides so, int causal, float scale,
+           void* stream) {
+    return fwd_common(q, k, v, o, lse, B, H, N, d, sq, sk, sv, so, causal, scale, nullptr, nullptr, 0, stream);
+}
+
+int fa_sparse_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                  int64_t N, int64_t d, fa_strides sq, fa_strides sk, fa_strides sv, fa_strides so,
+                  int64_t block_size, const int32_t* kv_offsets, const int32_t* kv_indices, int64_t nnz,
+                  int causal, float scale, void* stream) {
+    if (block_size != 128) return fail(FA_ERR_SHAPE, "block size %lld not supported (128)", (long long)block_size);
+    if (nnz < 0) return fail(FA_ERR_LIST, "negative nnz");
+    int st = check_sizes(B, H, N, d);
+    if (st) return st;
+    if (B == 0 || H == 0 || N == 0) return ok();
+    if (!kv_offsets) return fail(FA_ERR_NULL, "kv_offsets is NULL");
+    if (!kv_indices && nnz > 0) return fail(FA_ERR_NULL, "kv_indices is NULL");
+    // With nnz == 0 the kernels read no index; any valid pointer stands in for a NULL one.
+    return fwd_common(q, k, v, o, lse, B, H, N, d, sq, sk, sv, so, causal, scale, kv_offsets,
+                      kv_indices ? kv_indices : kv_offsets, nnz, stream);
+}
+
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+    (void)d;
+    if (B <= 0 || H <= 0 || N <= 0) return 0;
+    const size_t bytes = (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+    return (bytes + 255) & ~(size_t)255;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+           void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, fa_strides sq, fa_strides sk,
+           fa_strides sv, fa_strides so, fa_strides sdo, fa_strides sdq, fa_strides sdk, fa_strides sdv, int causal,
+           float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_sizes(B, H, N, d);
+    if (st) return st;
+    if (!std::isfinite(scale)) return fail(FA_ERR_ARG, "scale is not finite");
+    if (B == 0 || H == 0 || N == 0) return ok();
+    if ((st = check_tensor("q", q, sq)) || (st = check_tensor("k", k, sk)) || (st = check_tensor("v", v, sv)) ||
+        (st = check_tensor("o", o, so)) || (st = check_tensor("dout", dout, sdo)) ||
+        (st = check_tensor("dq", dq, sdq)) || (st = check_tensor("dk", dk, sdk)) ||
+        (st = check_tensor("dv", dv, sdv)))
+        return st;
+    if (!lse) return fail(FA_ERR_NULL, "lse is NULL");
+    if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(FA_ERR_LAYOUT, "lse is not 4-byte aligned");
+    const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
+    if (!workspace) return fail(FA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(FA_ERR_LAYOUT, "workspace is not 16-byte aligned");
+    if ((st = check_device())) return st;
+    fa::BwdArgs a;
+    a.q = view(q, sq);
+    a.k = view(k, sk);
+    a.v = view(v, sv);
+    a.o = view(o, so);
+    a.dout = view(dout, sdo);
+    a.lse = lse;
+    a.dq = dq; a.dqsb = sdq.b; a.dqsh = sdq.h; a.dqsn = sdq.n;
+    a.dk = dk; a.dksb = sdk.b; a.dksh = sdk.h; a.dksn = sdk.n;
+    a.dv = dv; a.dvsb = sdv.b; a.dvsh = sdv.h; a.dvsn = sdv.n;
+    a.delta = static_cast<float*>(workspace);
+    a.B = (int)B; a.H = (int)H; a.N = (int)N; a.d = (int)d;
+    a.causal = causal != 0;
+    a.scale = scale;
+    return launched(fa::launch_bwd(a, static_cast<hipStream_t>(stream)), "backward");
+}
+
+int fa_make_block_lists(int64_t n_blocks, int32_t window, int32_t stride, int causal, int rule, int32_t* offsets,
+                        int32_t* indices, int64_t cap, int64_t* nnz) {
+    if (n_blocks < 0 || n_blocks > kMaxDim) return fail(FA_ERR_SHAPE, "bad n_blocks %lld", (long long)n_blocks);
+    if (window < 0 || stride < 0) return fail(FA_ERR_ARG, "window and stride must be >= 0");
+    if (rule != 0 && rule != 1) return fail(FA_ERR_ARG, "rule must be 0 (strided) or 1 (fixed)");
+    if (!offsets || !nnz || (cap > 0 && !indices)) return fail(FA_ERR_NULL, "NULL output pointer");
+    int64_t count = 0;
+    offsets[0] = 0;
+    for (int64_t q = 0; q < n_blocks; ++q) {
+        const int64_t hi = causal ? q : n_blocks - 1;
+        const int64_t wlo = q - window < 0 ? 0 : q - window;
+        const int64_t whi = q + window < hi ? q + window : hi;
+        for (int64_t k = 0; k <= hi; ++k) {
+            bool keep = k >= wlo && k <= whi;
+            if (!keep && stride > 0) {
+                if (rule == 0) {
+                    const int64_t dist = q >= k ? q - k : k - q;
+                    keep = dist % stride == 0;
+                } else {
+                    keep = k % stride == 0;
+                }
+            }
+            if (keep) {
+                if (count < cap) indices[count] = (int32_t)k;
+                ++count;
+            }
+        }
+        if (count > INT32_MAX) return fail(FA_ERR_CAPACITY, "pattern exceeds int32 offsets");
+        offsets[q + 1] = (int32_t)count;
+    }
+    *nnz = count;
+    if (count > cap) return fail(FA_ERR_CAPACITY, "indices capacity %lld, %lld needed", (long long)cap, (long long)count);
+    return ok();
+}
+
+int fa_check_block_lists(const int32_t* offsets, const int32_t* indices, int64_t n_blocks, int64_t nnz, int causal) {
+    if (n_blocks < 0 || nnz < 0) return fail(FA_ERR_LIST, "negative n_blocks or nnz");
+    if (!offsets) return fail(FA_ERR_NULL, "offsets is NULL");
+    if (nnz > 0 && !indices) return fail(FA_ERR_NULL, "indices is NULL");
+    if (offsets[0] != 0) return fail(FA_ERR_LIST, "offsets[0] = %d, expected 0", offsets[0]);
+    for (int64_t q = 0; q < n_blocks; ++q) {
+        const int64_t lo = offsets[q], hi = offsets[q + 1];
+        if (hi < lo) return fail(FA_ERR_LIST, "offsets decrease at block %lld", (long long)q);
+        if (hi > nnz) return fail(FA_ERR_LIST, "offsets[%lld] = %lld exceeds nnz %lld", (long long)q + 1, (long long)hi, (long long)nnz);
+        for (int64_t t = lo; t < hi; ++t) {
+            const int64_t k = indices[t];
+            if (k < 0 || k >= n_blocks)
+                return fail(FA_ERR_LIST, "index %lld of block %lld out of range", (long long)k, (long long)q);
+            if (causal && k > q)
+                return fail(FA_ERR_LIST, "index %lld above causal query block %lld", (long long)k, (long long)q);
+            if (t > lo && indices[t - 1] >= k)
+                return fail(FA_ERR_LIST, "indices of block %lld not strictly ascending", (long long)q);
+        }
+    }
+    if (offsets[n_blocks] != nnz)
+        return fail(FA_ERR_LIST, "offsets[n_blocks] = %d differs from nnz %lld", offsets[n_blocks], (long long)nnz);
+    return ok();
+}
+
+const char* fa_status_str(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_NULL: return "FA_ERR_NULL";
+        case FA_ERR_SHAPE: return "FA_ERR_SHAPE";
+        case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM";
+        case FA_ERR_LAYOUT: return "FA_ERR_LAYOUT";
+        case FA_ERR_LIST: return "FA_ERR_LIST";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+        case FA_ERR_HIP: return "FA_ERR_HIP";
+        case FA_ERR_ARG: return "FA_ERR_ARG";
+        case FA_ERR_CAPACITY: return "FA_ERR_CAPACITY";
+        default: return "FA_ERR_UNKNOWN";
+    }
+}
+
+const char* fa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

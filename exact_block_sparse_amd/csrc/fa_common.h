@@ -1,0 +1,96 @@
+// Device-side building blocks shared by the forward and backward kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// D(32x32 fp32) += A(32x16 bf16) * B(16x32 bf16), one wave64.
+// Operand layout used throughout: lane l supplies row (A) / column (B) l % 32 and the
+// 8 k-values of k-group l / 32; the accumulator element r of lane l is row
+// 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row of the 32x32 accumulator held in element r by a lane of half `hf` (= lane / 32).
+__device__ __forceinline__ int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
+
+// Swap bits 2 and 3 of a row index in [0, 32). Loading A-operand row i from key
+// swz(i) makes the accumulator row order, read back as a B operand, name 8 consecutive
+// keys per lane: B element e of k-step s in half hf is key 16*s + 8*hf + e.
+__device__ __forceinline__ int swz(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+// Combine a value with the one held by the lane 32 positions away (the other half of the
+// wave), with a symmetric op: the two halves hold complementary keys of the same query.
+__device__ __forceinline__ float pair_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_min(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// 16-byte global load that yields zeros when `ok` is false (no access is made then).
+__device__ __forceinline__ u32x4 load16(const uint16_t* p, bool ok) {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    return ok ? *reinterpret_cast<const u32x4*>(p) : z;
+}
+
+// Pack eight fp32 values into an MFMA bf16 operand (round to nearest even).
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                        float a6, float a7) {
+    bf16x8 r;
+    r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+    r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+    return r;
+}
+
+// Workgroups are handed to the 8 XCDs round-robin. Map the hardware id so that the
+// logical ids an XCD receives are consecutive: neighbouring query blocks of one head then
+// run on the same XCD and share its L2 for the K/V stream.
+__device__ __forceinline__ int xcd_remap(int w, int G) {
+    constexpr int X = 8;
+    const int x = w % X, slot = w / X;
+    const int per = G / X, rem = G % X;
+    return x * per + (x < rem ? x : rem) + slot;
+}
+
+// Transpose four 16-byte rows (4 keys x 8 head-dim values, bf16) into eight 8-byte
+// columns (8 head-dim values x 4 keys) written at dst + c*row_stride, c = 0..7.
+__device__ __forceinline__ void store_transposed_4x8(uint16_t* dst, int row_stride, const u32x4& r0,
+                                                     const u32x4& r1, const u32x4& r2, const u32x4& r3) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        u32x2 even, odd;
+        even[0] = (r0[w] & 0xffffu) | (r1[w] << 16);
+        even[1] = (r2[w] & 0xffffu) | (r3[w] << 16);
+        odd[0] = (r0[w] >> 16) | (r1[w] & 0xffff0000u);
+        odd[1] = (r2[w] >> 16) | (r3[w] & 0xffff0000u);
+        *reinterpret_cast<u32x2*>(dst + (2 * w) * row_stride) = even;
+        *reinterpret_cast<u32x2*>(dst + (2 * w + 1) * row_stride) = odd;
+    }
+}
+
+}  // namespace fa

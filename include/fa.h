@@ -1,0 +1,193 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) tiled exact attention library, libfa.so.
+ *
+ * What the library computes. Exact multi-head attention O = softmax(Q K^T * scale + mask) V
+ * ("Flash MSA Attention Kernel Implementation: A Practical Guide for Production AI",
+ * section "Why Standard Attention Broke"), evaluated tile by tile with an online softmax
+ * (same page, section "The Flash Core: Tiling Over the Memory Hierarchy"), never writing
+ * the N x N score matrix. Masked keys are excluded (a -inf score, never 0: same page,
+ * FAQ on NaN debugging). Every call returns the exact result up to floating-point
+ * rounding: bf16 inputs, fp32 accumulation, bf16 outputs, fp32 log-sum-exp.
+ *
+ * Tensors. Q, K, V, O, dO, dQ, dK, dV are bf16 (bfloat16, round-to-nearest-even on write)
+ * device buffers of logical shape [B, H, N, d]. Element (b, h, n, c) lives at
+ *     ptr + b*stride.b + h*stride.h + n*stride.n + c          (strides in elements)
+ * so both (B,H,N,d) and (B,N,H,d) memory layouts are accepted (the pages use both:
+ * [num_heads, N, d] in page 1's CUDA kernel, (B, T, H, D_head) in "How to Use Flash MSA
+ * Kernels for Long Context", section "Step-by-Step"). Requirements (else FA_ERR_LAYOUT):
+ * the head dimension is contiguous; every pointer is 16-byte aligned; every stride is a
+ * multiple of 8 elements. LSE is fp32, contiguous [B, H, N], natural logarithm.
+ *
+ * Ownership and execution. The caller allocates and owns every buffer (device memory for
+ * tensors, lists and workspace; host memory only where a parameter says "host"). The
+ * library keeps no state between calls except a per-thread error detail string, allocates
+ * nothing, launches asynchronously on the given HIP stream (a hipStream_t passed as
+ * void*; NULL is the default stream) and never synchronises: outputs are valid once the
+ * stream has reached the launches. There is no fallback path of any kind: a call either
+ * launches the gfx950 kernels or returns an error status. Calls are thread-safe.
+ *
+ * Errors. Every entry point returns FA_OK (0) or one of the FA_ERR_* codes below.
+ * Arguments are validated on the host before any HIP call; fa_last_error() gives a
+ * human-readable detail for the calling thread's most recent failure.
+ * Sizes B, H or N equal to 0 are a valid empty problem: FA_OK, nothing launched.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define FA_API __attribute__((visibility("default")))
+#else
+#define FA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_OK 0
+#define FA_ERR_NULL 1       /* a required pointer is NULL                                 */
+#define FA_ERR_SHAPE 2      /* B, H or N negative; sparse block size unsupported            */
+#define FA_ERR_HEADDIM 3    /* d is not 64 or 128                                           */
+#define FA_ERR_LAYOUT 4     /* d not contiguous, pointer or stride not 16-byte aligned      */
+#define FA_ERR_LIST 5       /* block lists fail fa_check_block_lists (host checks only)     */
+#define FA_ERR_WORKSPACE 6  /* backward workspace missing or too small                      */
+#define FA_ERR_HIP 7        /* HIP runtime error (no device, launch failure, ...)           */
+#define FA_ERR_ARG 8        /* other invalid argument (scale not finite, bad rule, ...)     */
+#define FA_ERR_CAPACITY 9   /* a host output array is too small                             */
+
+/* Element strides of one [B, H, N, d] tensor; the d stride is 1. */
+typedef struct fa_strides {
+    int64_t b;
+    int64_t h;
+    int64_t n;
+} fa_strides;
+
+/*
+ * fa_fwd - dense or causal attention forward with log-sum-exp write-out.
+ *
+ * Defined by the forward tile loop of "Flash MSA Attention Kernel Implementation: A
+ * Practical Guide for Production AI" (sections "The Flash Core: Tiling Over the Memory
+ * Hierarchy" and "Code: A Complete Flash Attention Forward Kernel in CUDA"): for each
+ * query row i, O_i = sum_j P_ij V_j with P_ij = exp(S_ij - m_i) / l_i over the allowed
+ * keys j, S = scale * Q K^T. With causal != 0 a key j is allowed only if j <= i (a key
+ * after the query is masked). The same page stores the per-row max m and sum l for the
+ * backward; this library stores their combination LSE_i = m_i + ln(l_i).
+ *
+ * q, k, v : device bf16, logical [B, H, N, d], strides sq, sk, sv.
+ * o       : device bf16 output, logical [B, H, N, d], strides so (may alias nothing else).
+ * lse     : device fp32 output, contiguous [B, H, N].
+ * B, H, N : sizes (>= 0). N may be any value; there is no tile-multiple requirement.
+ * d       : head dimension, 64 or 128.
+ * causal  : 0 = full attention, nonzero = causal (j <= i).
+ * scale   : score multiplier, any finite float (1/sqrt(d) is the usual choice; the pages
+ *           use it in every kernel). Not finite -> FA_ERR_ARG.
+ * stream  : hipStream_t (NULL = default stream).
+ */
+FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int64_t B, int64_t H, int64_t N, int64_t d,
+           fa_strides sq, fa_strides sk, fa_strides sv, fa_strides so,
+           int causal, float scale, void* stream);
+
+/*
+ * fa_sparse_fwd - block-sparse (Flash-MSA) attention forward with log-sum-exp write-out.
+ *
+ * Defined in "How Does Flash-MSA Sparse Attention Work", section "How Flash-MSA Sparse
+ * Attention Works": the sequence is cut into blocks of block_size tokens and a
+ * precomputed index list names, for every query block, the key blocks it attends to;
+ * the mask is applied inside the tile loop, so only listed key blocks enter the online
+ * softmax and unlisted ones are never loaded. The result is exact attention over the
+ * allowed keys: key j is allowed for query i iff block(j) is listed for block(i) and,
+ * with causal != 0, j <= i. A query row with no allowed key gets O = 0 and LSE = -inf.
+ *
+ * block_size : tokens per block; this version supports 128 (FA_ERR_SHAPE otherwise).
+ *              The last block may be partial (N need not be a multiple).
+ * kv_offsets : device int32 [nb + 1], nb = ceil(N / block_size). Query block qb lists
+ *              kv_indices[kv_offsets[qb] .. kv_offsets[qb+1]).
+ * kv_indices : device int32 [nnz], key block numbers, ascending and unique per query block.
+ * nnz        : number of elements of kv_indices.
+ * The lists are shared by every batch and head. They must pass fa_check_block_lists;
+ * the kernels stay in bounds whatever the list contents (offsets are clamped to
+ * [0, nnz], indices outside [0, nb), and with causal masking indices above the query
+ * block, are skipped), but duplicated or unsorted entries give undefined results.
+ * Other arguments as in fa_fwd.
+ */
+FA_API int fa_sparse_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int64_t B, int64_t H, int64_t N, int64_t d,
+                  fa_strides sq, fa_strides sk, fa_strides sv, fa_strides so,
+                  int64_t block_size, const int32_t* kv_offsets, const int32_t* kv_indices,
+                  int64_t nnz, int causal, float scale, void* stream);
+
+/*
+ * fa_bwd_workspace_bytes - device workspace fa_bwd needs: one fp32 per query row
+ * (the row dot products D_i = dO_i . O_i), B*H*N*4 bytes rounded up to 256.
+ */
+FA_API size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
+
+/*
+ * fa_bwd - attention backward by recomputation from the stored log-sum-exp.
+ *
+ * Defined in "Flash MSA Attention Kernel Implementation: A Practical Guide for Production
+ * AI", section "The Backward Pass: The Real Beast": the forward keeps O and the softmax
+ * statistics instead of the N x N matrix; the backward recomputes P_ij = exp(S_ij - LSE_i)
+ * tile by tile and forms dP = dO V^T, dS = P o (dP - D) with D_i = sum_j P_ij dP_ij
+ * (= dO_i . O_i), dV = P^T dO, and, through S = scale * Q K^T, dQ = scale * dS K and
+ * dK = scale * dS^T Q. Accumulation is fp32; dq, dk, dv are written as bf16.
+ *
+ * q, k, v, o, dout : device bf16 inputs (o and lse are the forward's outputs for q, k, v).
+ * lse              : device fp32 [B, H, N] from fa_fwd with the same causal and scale.
+ * dq, dk, dv       : device bf16 outputs, logical [B, H, N, d].
+ * workspace        : device buffer of at least fa_bwd_workspace_bytes(...) bytes,
+ *                    16-byte aligned; its contents on entry are ignored.
+ * Other arguments as in fa_fwd. The kernels are deterministic (no atomics).
+ */
+FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv,
+           int64_t B, int64_t H, int64_t N, int64_t d,
+           fa_strides sq, fa_strides sk, fa_strides sv, fa_strides so, fa_strides sdo,
+           fa_strides sdq, fa_strides sdk, fa_strides sdv,
+           int causal, float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_make_block_lists - host generator of the block-sparse pattern used with fa_sparse_fwd.
+ *
+ * "How Does Flash-MSA Sparse Attention Work", section "How Flash-MSA Sparse Attention
+ * Works", names a local window of +-W positions and the fixed "strided" pattern of Child
+ * et al. (2019). At block granularity, query block q lists the union of
+ *   window : key blocks k with |q - k| <= window (k <= q when causal), and
+ *   stride : rule 0 ("strided") key blocks with |q - k| divisible by stride,
+ *            rule 1 ("fixed")   key blocks with k divisible by stride
+ *            (k <= q when causal; stride 0 disables the strided part),
+ * sorted ascending without repeats, in CSR form.
+ *
+ * offsets : host int32 [n_blocks + 1] output.
+ * indices : host int32 [cap] output. If the pattern needs more than cap entries the
+ *           call returns FA_ERR_CAPACITY and *nnz holds the needed count.
+ * nnz     : host output, number of entries written (or needed).
+ */
+FA_API int fa_make_block_lists(int64_t n_blocks, int32_t window, int32_t stride, int causal, int rule,
+                        int32_t* offsets, int32_t* indices, int64_t cap, int64_t* nnz);
+
+/*
+ * fa_check_block_lists - host validation of CSR block lists (all pointers host).
+ * FA_OK iff offsets[0] == 0, offsets are non-decreasing, offsets[n_blocks] == nnz, every
+ * index is in [0, n_blocks), each query block's indices are strictly ascending, and,
+ * when causal != 0, no index exceeds its query block. Otherwise FA_ERR_LIST (FA_ERR_NULL
+ * for null pointers with n_blocks > 0).
+ */
+FA_API int fa_check_block_lists(const int32_t* offsets, const int32_t* indices, int64_t n_blocks,
+                         int64_t nnz, int causal);
+
+/* Static string naming a status code ("FA_OK", "FA_ERR_SHAPE", ...). Never NULL. */
+FA_API const char* fa_status_str(int status);
+
+/* Detail of the calling thread's most recent failed call ("" if none). Never NULL. */
+FA_API const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

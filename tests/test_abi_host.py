@@ -1,0 +1,156 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+The library loads, exports every entry point include/fa.h declares, rejects malformed
+arguments with the documented status before any HIP call, and its block-list generator
+agrees element for element with the oracle's own implementation of the pattern.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import exact_block_sparse_amd as fa
+    return fa
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    return sorted(set(re.findall(r"FA_API\s+[\w\s\*]+?\b(fa_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(fa):
+    declared = declared_functions()
+    assert set(declared) == set(fa.EXPORTS), declared
+    so = ctypes.CDLL(fa.LIB_PATH)
+    for name in declared:
+        assert hasattr(so, name), name
+
+
+def test_library_is_built_for_gfx950(fa):
+    with open(fa.LIB_PATH, "rb") as f:
+        blob = f.read()
+    assert b"gfx950" in blob
+
+
+def test_status_strings(fa):
+    for code, name in fa.FA_STATUS.items():
+        assert fa.status_str(code) == name
+    assert fa.status_str(12345) == "FA_ERR_UNKNOWN"
+
+
+S = None
+
+
+def strides(b, h, n):
+    from exact_block_sparse_amd import Strides
+    return Strides(b, h, n)
+
+
+def call_fwd(fa, q=16, k=16, v=16, o=16, lse=16, B=1, H=1, N=64, d=128, st=(8192, 8192, 128),
+             causal=0, scale=0.1):
+    s = strides(*st)
+    return fa.lib.fa_fwd(ctypes.c_void_p(q), ctypes.c_void_p(k), ctypes.c_void_p(v), ctypes.c_void_p(o),
+                         ctypes.c_void_p(lse), B, H, N, d, s, s, s, s, causal, scale, None)
+
+
+def test_fwd_argument_errors_before_any_hip_call(fa):
+    # pointers are fake: every case must be rejected on the host before a launch
+    assert call_fwd(fa, q=0) == 1                    # FA_ERR_NULL
+    assert call_fwd(fa, lse=0) == 1
+    assert call_fwd(fa, N=-1) == 2                   # FA_ERR_SHAPE
+    assert call_fwd(fa, d=96) == 3                   # FA_ERR_HEADDIM
+    assert call_fwd(fa, q=24) == 4                   # misaligned pointer -> FA_ERR_LAYOUT
+    assert call_fwd(fa, st=(8192, 8192, 100)) == 4   # stride not a multiple of 8
+    assert call_fwd(fa, scale=float("inf")) == 8     # FA_ERR_ARG
+    assert "scale" in fa.lib.fa_last_error().decode()
+    assert call_fwd(fa, q=0, N=0) == 0               # empty problem: OK, nothing launched
+    assert call_fwd(fa, q=0, B=0) == 0
+
+
+def test_sparse_argument_errors(fa):
+    s = strides(8192, 8192, 128)
+    vp = ctypes.c_void_p
+    f = fa.lib.fa_sparse_fwd
+    args = lambda **kw: [vp(16)] * 5 + [1, 1, 256, 128, s, s, s, s, kw.get("bs", 128), vp(kw.get("off", 16)),
+                                       vp(kw.get("idx", 16)), kw.get("nnz", 4), 1, 0.1, None]
+    assert f(*args(bs=64)) == 2
+    assert f(*args(off=0)) == 1
+    assert f(*args(idx=0)) == 1
+    assert f(*args(nnz=-1)) == 5
+
+
+def test_bwd_workspace_rules(fa):
+    assert fa.bwd_workspace_bytes(2, 32, 8192, 128) == 2 * 32 * 8192 * 4
+    assert fa.bwd_workspace_bytes(1, 1, 3, 64) == 256
+    assert fa.bwd_workspace_bytes(0, 1, 3, 64) == 0
+    s = strides(8192, 8192, 128)
+    vp = ctypes.c_void_p
+    base = [vp(16)] * 9 + [1, 1, 64, 128] + [s] * 8 + [0, 0.1]
+    assert fa.lib.fa_bwd(*base, vp(0), 0, None) == 6            # no workspace
+    assert fa.lib.fa_bwd(*base, vp(16), 255, None) == 6          # too small
+    assert fa.lib.fa_bwd(*base, vp(24), 4096, None) == 4         # misaligned
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful where no GPU is present")
+def test_no_device_is_reported_not_faked(fa):
+    assert call_fwd(fa) == 7                          # FA_ERR_HIP: no device, nothing ran
+    assert "device" in fa.lib.fa_last_error().decode()
+
+
+@pytest.mark.parametrize("nb,window,stride,causal,rule", [
+    (1024, 8, 16, True, "strided"), (1024, 8, 16, True, "fixed"), (1, 8, 16, True, "strided"),
+    (50, 3, 7, False, "strided"), (50, 0, 0, True, "strided"), (33, 40, 5, False, "fixed")])
+def test_block_lists_equal_oracle(fa, nb, window, stride, causal, rule):
+    off, idx = fa.make_block_lists(nb, window, stride, causal=causal, rule=rule)
+    off2, idx2 = oracle.block_lists(nb, window, stride, causal=causal, rule=rule)
+    assert off.dtype == np.int32 and idx.dtype == np.int32
+    assert np.array_equal(off, off2) and np.array_equal(idx, idx2)
+    fa.check_block_lists(off, idx, nb, causal=causal)
+
+
+def test_block_lists_128k_totals(fa):
+    off, idx = fa.make_block_lists(1024, 8, 16)
+    assert int(off[-1]) == 41436 and int(np.diff(off).max()) == 72
+
+
+def test_check_block_lists_rejects_malformed(fa):
+    off, idx = fa.make_block_lists(20, 2, 4)
+    bad = []
+    i2 = idx.copy(); i2[5] = 25; bad.append((off, i2))                       # out of range
+    i3 = idx.copy(); i3[1], i3[2] = i3[2], i3[1]; bad.append((off, i3))      # not ascending (block 2)
+    o4 = off.copy(); o4[0] = 1; bad.append((o4, idx))                        # offsets[0] != 0
+    o5 = off.copy(); o5[3] = o5[4] + 1; bad.append((o5, idx))                # decreasing
+    for o, i in bad:
+        with pytest.raises(fa.FaError) as e:
+            fa.check_block_lists(o, i, 20, causal=True)
+        assert e.value.name == "FA_ERR_LIST"
+    # above the causal diagonal is fine without causal masking, rejected with it
+    o6 = np.array([0, 2], dtype=np.int32)
+    i6 = np.array([0, 0], dtype=np.int32)
+    with pytest.raises(fa.FaError):
+        fa.check_block_lists(o6, i6, 1)
+    fa.check_block_lists(np.array([0, 1, 2], np.int32), np.array([1, 0], np.int32), 2, causal=False)
+    with pytest.raises(fa.FaError):
+        fa.check_block_lists(np.array([0, 1, 2], np.int32), np.array([1, 0], np.int32), 2, causal=True)
+
+
+def test_make_block_lists_capacity(fa):
+    off = np.zeros(11, np.int32)
+    idx = np.zeros(3, np.int32)
+    nnz = ctypes.c_int64(0)
+    p = ctypes.POINTER(ctypes.c_int32)
+    st = fa.lib.fa_make_block_lists(10, 2, 4, 1, 0, off.ctypes.data_as(p), idx.ctypes.data_as(p), 3,
+                                    ctypes.byref(nnz))
+    assert st == 9 and nnz.value > 3
+    assert fa.lib.fa_make_block_lists(10, -1, 4, 1, 0, off.ctypes.data_as(p), idx.ctypes.data_as(p), 3,
+                                      ctypes.byref(nnz)) == 8

@@ -1,0 +1,277 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Small cases are compared element by element (they span several tiles and ragged tails);
+the five benchmark workloads are compared on sampled rows at their full sizes, in the
+launch configuration the bench times. Tolerances: max-abs 2e-2 on O, dQ, dK, dV and
+1e-3 on LSE; block lists exactly.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import TOL_LSE, TOL_OUT, assert_close, assert_finite, f64, sample_rows, scale_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write(f"\n[gpu-case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+
+
+@pytest.fixture(scope="module")
+def fa():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import exact_block_sparse_amd as fa
+    return fa
+
+
+def to_dev(t):
+    return t.to("cuda")
+
+
+def small_inputs(B, H, N, d, layout="bhnd", seed=0, sigma=1.0, grad=False):
+    w = W.small(B, H, N, d, layout=layout, seed=seed, sigma=sigma)
+    return W.make_inputs(w, with_grad=grad)
+
+
+# ----------------------------------------------------------------------------- forward, small
+FWD_CASES = [
+    # B, H, N, d, causal, layout, scale (None = 1/sqrt(d))
+    (1, 1, 64, 64, False, "bhnd", None),
+    (1, 1, 1, 128, False, "bhnd", None),
+    (1, 1, 1, 64, True, "bhnd", None),
+    (1, 2, 200, 128, True, "bhnd", None),
+    (2, 2, 256, 64, True, "bnhd", None),
+    (1, 1, 129, 128, True, "bhnd", None),
+    (1, 3, 333, 128, False, "bnhd", None),
+    (2, 1, 640, 128, True, "bhnd", None),
+    (1, 2, 300, 64, False, "bhnd", -0.2),
+    (1, 1, 190, 128, True, "bhnd", 0.0),
+    (1, 1, 257, 128, True, "bhnd", 0.9),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,layout,scale", FWD_CASES)
+def test_fwd_small(fa, B, H, N, d, causal, layout, scale):
+    x = small_inputs(B, H, N, d, layout, seed=N + d)
+    sc = scale_for(d) if scale is None else float(np.float32(scale))
+    q, k, v = (to_dev(x[n]) for n in "qkv")
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    assert o.stride() == q.stride()
+    O_ref, L_ref = oracle.attention_forward(x["q"], x["k"], x["v"], causal=causal, scale=sc)
+    assert_close("O", o, O_ref, TOL_OUT)
+    assert_close("LSE", lse, L_ref, TOL_LSE)
+
+
+def test_fwd_empty_is_noop(fa):
+    q = torch.zeros((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
+    o, lse = fa.fwd(q, q, q, causal=True)
+    assert o.shape == (1, 2, 0, 128) and lse.shape == (1, 2, 0)
+
+
+def test_fwd_deterministic(fa):
+    x = small_inputs(1, 2, 1000, 128, seed=7)
+    q, k, v = (to_dev(x[n]) for n in "qkv")
+    o1, l1 = fa.fwd(q, k, v, causal=True)
+    o2, l2 = fa.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_fwd_rejects_bad_arguments(fa):
+    q = torch.zeros((1, 1, 64, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FaError) as e:
+        fa.fwd(q, q, q)
+    assert e.value.name == "FA_ERR_HEADDIM"
+    q = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FaError) as e:
+        fa.fwd(q, q, q, scale=float("nan"))
+    assert e.value.name == "FA_ERR_ARG"
+
+
+# ----------------------------------------------------------------------------- sparse, small
+def test_sparse_lists_match_oracle_rule(fa):
+    for nb, w, s, rule in ((1024, 8, 16, "strided"), (1024, 8, 16, "fixed"), (37, 2, 3, "strided")):
+        off, idx = fa.make_block_lists(nb, w, s, causal=True, rule=rule)
+        off2, idx2 = oracle.block_lists(nb, w, s, causal=True, rule=rule)
+        assert np.array_equal(off, off2) and np.array_equal(idx, idx2)
+
+
+SPARSE_CASES = [
+    # B, H, N, d, causal, window, stride, rule
+    (1, 2, 128 * 13 + 37, 128, True, 2, 3, "strided"),
+    (2, 1, 128 * 9, 64, True, 1, 4, "fixed"),
+    (1, 1, 128 * 7 + 1, 128, False, 1, 3, "strided"),
+    (1, 2, 128 * 6, 128, True, 10, 0, "strided"),     # window covers everything: causal dense
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,window,stride,rule", SPARSE_CASES)
+def test_sparse_small(fa, B, H, N, d, causal, window, stride, rule):
+    x = small_inputs(B, H, N, d, seed=N)
+    nb = (N + 127) // 128
+    off, idx = fa.make_block_lists(nb, window, stride, causal=causal, rule=rule)
+    q, k, v = (to_dev(x[n]) for n in "qkv")
+    o, lse = fa.sparse_fwd(q, k, v, off, idx, causal=causal)
+    torch.cuda.synchronize()
+    sp = dict(block=128, window=window, stride=stride, rule=rule)
+    O_ref, L_ref = oracle.attention_forward(x["q"], x["k"], x["v"], causal=causal, scale=scale_for(d), sparse=sp)
+    assert_close("O", o, O_ref, TOL_OUT)
+    assert_close("LSE", lse, L_ref, TOL_LSE)
+    if window >= nb and causal:
+        o2, l2 = fa.fwd(q, k, v, causal=True)
+        torch.cuda.synchronize()
+        assert_close("O(dense)", o, f64(o2), TOL_OUT)
+
+
+def test_sparse_hand_lists_with_empty_block(fa):
+    N, d = 128 * 5, 128
+    x = small_inputs(1, 1, N, d, seed=3)
+    off = np.array([0, 1, 1, 3, 5, 6], dtype=np.int32)       # query block 1 lists nothing
+    idx = np.array([0, 0, 2, 1, 3, 4], dtype=np.int32)
+    q, k, v = (to_dev(x[n]) for n in "qkv")
+    o, lse = fa.sparse_fwd(q, k, v, off, idx, causal=True)
+    torch.cuda.synchronize()
+    sp = dict(block=128, offsets=off, indices=idx)
+    O_ref, L_ref = oracle.attention_forward(x["q"], x["k"], x["v"], causal=True, scale=scale_for(d), sparse=sp)
+    assert_close("O", o, O_ref, TOL_OUT)
+    assert_close("LSE", lse, L_ref, TOL_LSE)
+    assert bool(torch.isneginf(lse[0, 0, 128:256]).all())
+    assert bool((o[0, 0, 128:256] == 0).all())
+
+
+def test_sparse_device_lists_out_of_range_entries_are_skipped(fa):
+    # Entries the kernels must skip without touching memory: a key block past the end and,
+    # under causal masking, one above the query block. Offsets past nnz are clamped.
+    N, d = 128 * 3, 64
+    x = small_inputs(1, 1, N, d, seed=4)
+    off = torch.tensor([0, 2, 4, 99], dtype=torch.int32, device="cuda")
+    idx = torch.tensor([0, 7, 1, 2, 0, 2], dtype=torch.int32, device="cuda")
+    q, k, v = (to_dev(x[n]) for n in "qkv")
+    o, lse = fa.sparse_fwd(q, k, v, off, idx, causal=True)
+    torch.cuda.synchronize()
+    # what remains: block 0 -> {0}; block 1 -> {1} (2 is above it); block 2 -> {0, 2}
+    sp = dict(block=128, offsets=np.array([0, 1, 2, 4]), indices=np.array([0, 1, 0, 2]))
+    O_ref, L_ref = oracle.attention_forward(x["q"], x["k"], x["v"], causal=True, scale=scale_for(d), sparse=sp)
+    assert_close("O", o, O_ref, TOL_OUT)
+    assert_close("LSE", lse, L_ref, TOL_LSE)
+
+
+# ----------------------------------------------------------------------------- backward, small
+BWD_CASES = [
+    (1, 1, 64, 64, False, "bhnd"),
+    (1, 2, 200, 128, True, "bhnd"),
+    (2, 1, 256, 64, True, "bnhd"),
+    (1, 1, 1, 128, True, "bhnd"),
+    (1, 2, 333, 128, False, "bhnd"),
+    (1, 1, 520, 128, True, "bnhd"),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,layout", BWD_CASES)
+def test_bwd_small(fa, B, H, N, d, causal, layout):
+    x = small_inputs(B, H, N, d, layout, seed=N + 1, grad=True)
+    sc = scale_for(d)
+    q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=sc)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    dQ, dK, dV = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], causal=causal, scale=sc)
+    assert_close("dQ", dq, dQ, TOL_OUT)
+    assert_close("dK", dk, dK, TOL_OUT)
+    assert_close("dV", dv, dV, TOL_OUT)
+
+
+def test_bwd_deterministic(fa):
+    x = small_inputs(1, 2, 700, 128, seed=9, grad=True)
+    q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    a = fa.bwd(q, k, v, o, lse, do, causal=True)
+    b = fa.bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    for x1, x2 in zip(a, b):
+        assert torch.equal(x1, x2)
+
+
+# ----------------------------------------------------------------------------- benchmark workloads
+def _fwd_workload(fa, key, n_heads_checked=2, extra_rows=24):
+    w = W.WORKLOADS[key]
+    x = W.make_inputs(w)
+    q, k, v = (to_dev(x[n]) for n in "qkv")
+    if w.layout == "bnhd":
+        assert q.stride(2) == w.H * w.d     # the BNHD layout survives the copy
+    if w.sparse:
+        nb = (w.N + 127) // 128
+        off, idx = fa.make_block_lists(nb, w.sparse["window"], w.sparse["stride"], causal=True,
+                                       rule=w.sparse["rule"])
+        o, lse = fa.sparse_fwd(q, k, v, off, idx, causal=w.causal, scale=w.scale)
+    else:
+        o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert_finite("O", o)
+    assert_finite("LSE", lse)
+    rng = np.random.default_rng(w.seed)
+    heads = [(0, 0), (w.B - 1, w.H - 1)][:n_heads_checked]
+    rows = sample_rows(w.N, 128 if w.N > 128 else w.N, rng, extra=extra_rows)
+    if w.N > 8192:   # keep the oracle's work to seconds: every block's edges would be thousands of rows
+        rows = np.unique(np.concatenate([rows[:: max(1, len(rows) // 96)], rows[-4:]]))
+    O_ref, L_ref = oracle.attention_forward(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale,
+                                            sparse=w.sparse, rows=rows, heads=heads)
+    for (b, h) in heads:
+        assert_close(f"O[{b},{h}]", o[b, h, rows], O_ref[b, h, rows], TOL_OUT)
+        assert_close(f"LSE[{b},{h}]", lse[b, h, rows], L_ref[b, h, rows], TOL_LSE)
+
+
+def test_workload_dense_n512_d64_full(fa):
+    w = W.WORKLOADS["dense_n512_d64"]
+    x = W.make_inputs(w)
+    q, k, v = (to_dev(x[n]) for n in "qkv")
+    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention_forward(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale)
+    assert_close("O", o, O_ref, TOL_OUT)
+    assert_close("LSE", lse, L_ref, TOL_LSE)
+
+
+def test_workload_causal_b4h32_n4k_bnhd(fa):
+    _fwd_workload(fa, "causal_b4h32_n4k_bnhd")
+
+
+def test_workload_causal_h32_n32k(fa):
+    _fwd_workload(fa, "causal_h32_n32k")
+
+
+def test_workload_sparse_h16_n128k(fa):
+    _fwd_workload(fa, "sparse_h16_n128k")
+
+
+def test_workload_bwd_b2h32_n8k(fa):
+    w = W.WORKLOADS["bwd_b2h32_n8k"]
+    x = W.make_inputs(w)
+    q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    for name, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert_finite(name, t)
+    # one head in full: every row of dQ, dK, dV against the oracle's own backward
+    b, h = 1, 17
+    dQ, dK, dV = oracle.attention_backward(x["q"][b:b + 1, h:h + 1], x["k"][b:b + 1, h:h + 1],
+                                           x["v"][b:b + 1, h:h + 1], x["do"][b:b + 1, h:h + 1],
+                                           causal=True, scale=w.scale)
+    assert_close("dQ", dq[b:b + 1, h:h + 1], dQ, TOL_OUT)
+    assert_close("dK", dk[b:b + 1, h:h + 1], dK, TOL_OUT)
+    assert_close("dV", dv[b:b + 1, h:h + 1], dV, TOL_OUT)
+    # sampled dQ rows of another head
+    rows = sample_rows(w.N, 128, np.random.default_rng(5), extra=8)[::8]
+    ref = oracle.backward_rows_dq(x["q"], x["k"], x["v"], x["do"], causal=True, scale=w.scale, b=0, h=3,
+                                  rows=rows)
+    assert_close("dQ rows", dq[0, 3, rows], np.stack([ref[int(r)] for r in rows]), TOL_OUT)
