@@ -194,7 +194,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads", default="all", choices=["all", "headline"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes 5 times (to scale "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration // 2
+        src_t = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst_t = torch.empty_like(src_t)
+        for _ in range(5):
+            dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 2 * n, "launches": 5}), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (heads and sequence "
               "shards are independent per GPU; see the design notes). Run with --gpus 1.", file=sys.stderr)

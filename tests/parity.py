@@ -25,7 +25,8 @@ def stats(got: np.ndarray, ref: np.ndarray) -> dict:
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     both_inf = np.isinf(got) & np.isinf(ref) & (np.sign(got) == np.sign(ref))
-    diff = np.where(both_inf, 0.0, np.abs(got - ref))
+    with np.errstate(invalid="ignore"):
+        diff = np.where(both_inf, 0.0, np.abs(got - ref))
     fin = np.isfinite(ref)
     denom = np.maximum(np.abs(ref), 1e-6)
     return dict(
