@@ -93,4 +93,35 @@ __device__ __forceinline__ void store_transposed_4x8(uint16_t* dst, int row_stri
     }
 }
 
+
+// Raw buffer resource over [base, base + bytes): loads at byte offsets >= bytes return 0
+// without touching memory (the hardware range check), which gives zero-filled tails.
+// Word 3 is the gfx9-family raw-buffer format (32-bit data format, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+// Bytes of rows [r0, n) of a matrix with row stride `sn` elements and `d` bf16 columns,
+// capped to `rows` rows; the cap keeps the value well inside 32 bits.
+__device__ __forceinline__ uint32_t rows_bytes(int r0, int n, int64_t sn, int d, int rows) {
+    int last = n - 1 - r0;
+    if (last >= rows) last = rows - 1;
+    if (last < 0) return 0u;
+    return (uint32_t)(((int64_t)last * sn + d) * 2);
+}
+
+// ds_read_b64_tr_b16 (gfx950): each lane supplies the LDS address of 4 consecutive bf16.
+// Within every group of 16 lanes, lane i receives element (i % 4) of the chunks addressed
+// by lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4. So if lane j of a group addresses
+// M[k0 + j/4][c0 + 4*(j%4)] of a row-major matrix, lane i receives M[k0 .. k0+3][c0 + i]:
+// a column, i.e. the transposed operand, without a transposing store.
+__device__ __forceinline__ u32x2 lds_read_tr4(const uint16_t* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (s16x4 __attribute__((address_space(3)))*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
 }  // namespace fa
