@@ -12,31 +12,34 @@
 // Works"): unlisted blocks are never loaded and never enter the softmax.
 //
 // MI355X mapping (design of this file, not the pages'):
-// * a workgroup is 4 wave64s; each wave owns QB blocks of 32 query rows (QB = 1: 128 rows
-//   per workgroup, two workgroups per CU; QB = 2: 256 rows, one workgroup per CU, and every
-//   K/V operand read from LDS feeds two MFMAs);
-// * key/value tiles of 64 keys are staged through LDS, double-buffered, with raw buffer
-//   loads whose hardware range check zero-fills rows past the sequence end; K and V are
-//   both stored row-major; P.V reads its V^T operands with the transposing LDS read
-//   ds_read_b64_tr_b16; row paddings keep reads and writes free of bank conflicts;
-// * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16, so the 32
-//   scores of a query over a 32-key block sit in one lane and its partner lane 32 away: the
-//   row max needs one cross-half exchange (v_permlane32_swap), the row sum none until the end;
+// * each wave64 owns 32 query rows. Scores are computed transposed, S^T = K Q^T, with
+//   v_mfma_f32_32x32x16_bf16, so the 32 scores of a query over a 32-key block sit in one
+//   lane and its partner lane 32 away: the row max needs one cross-half exchange
+//   (v_permlane32_swap) and the row sum none until the end;
+// * key/value tiles of 64 keys are staged through LDS with raw buffer loads whose
+//   hardware range check zero-fills rows past the sequence end. K and V are stored
+//   row-major; P.V reads its V^T operands with the transposing LDS read
+//   ds_read_b64_tr_b16. Row paddings (272-byte K rows, 320-byte V rows) keep every LDS
+//   read and write free of bank conflicts on the 64-bank LDS;
 // * the running max is raised only when a tile's max exceeds it by more than 2^8 (in the
 //   exp2 domain): probabilities then stay below 256 and the O rescale becomes rare. The
 //   result is the same function; only the reference point of the exponentials moves;
 // * O^T = V^T P^T accumulates in fp32 registers; P is rounded to bf16 only as an MFMA
 //   operand; exp is computed as exp2 with scale*log2(e) folded into one FMA;
+// * dense kernel ("ping-pong"): 8 waves and 256 query rows per workgroup, in two groups of
+//   four that alternate phase by phase: while one group runs its matrix products (P.V of
+//   the previous tile, then S of the current one) the other runs its softmax on the vector
+//   ALU. Each SIMD holds one wave of each group, so the MFMA pipe and the VALU work at the
+//   same time. Tiles cycle through three LDS buffers so loads run two tiles ahead;
+// * sparse kernel: 4 waves and one 128-row block per workgroup (the list granularity),
+//   two workgroups per CU, each step in one go;
 // * the LSE is written in natural log, O as bf16.
-#include <cstdlib>
-
 #include "fa_common.h"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kBK = 64;            // keys per pipeline step
 constexpr int kSparseBlock = 128;
 constexpr float kRescaleSlack = 8.0f;   // log2 of the largest probability allowed before a rescale
@@ -49,7 +52,6 @@ struct Cfg {
     static constexpr int VEL = kBK * VS;
     static constexpr int BUF = KEL + VEL;        // elements per pipeline stage
     static constexpr int CR = D / 8;             // 16-byte chunks per row
-    static constexpr int KCH = kBK * CR / kThreads;
     static constexpr int KSTEPS = D / 16;        // MFMA k-steps over the head dimension
     static constexpr int CB = D / 32;            // 32-wide head-dimension blocks of O
     static_assert((BUF * 2) % 16 == 0, "stage size must keep 16-byte alignment");
@@ -71,20 +73,22 @@ struct Params {
 };
 
 // Per-thread staging of one K/V step: 16-byte row chunks of K and V.
-template <int D>
+template <int D, int NT>
 struct Stage {
     using C = Cfg<D>;
-    u32x4 k[C::KCH];
-    u32x4 v[C::KCH];
-    uint32_t koff[C::KCH];   // byte offsets (relative to the step's first row), fixed per thread
-    uint32_t voff[C::KCH];
-    int klds[C::KCH];        // LDS element offsets of the chunks
-    int vlds[C::KCH];
+    static constexpr int KCH = kBK * C::CR / NT;
+    static_assert(KCH >= 1 && kBK * C::CR % NT == 0, "chunks must divide evenly");
+    u32x4 k[KCH];
+    u32x4 v[KCH];
+    uint32_t koff[KCH];   // byte offsets (relative to the step's first row), fixed per thread
+    uint32_t voff[KCH];
+    int klds[KCH];        // LDS element offsets of the chunks
+    int vlds[KCH];
 
     __device__ void init(int tid, int64_t ksn, int64_t vsn) {
 #pragma unroll
-        for (int j = 0; j < C::KCH; ++j) {
-            const int id = tid + j * kThreads;
+        for (int j = 0; j < KCH; ++j) {
+            const int id = tid + j * NT;
             const int row = id / C::CR, ch = id % C::CR;
             koff[j] = (uint32_t)(((int64_t)row * ksn + 8 * ch) * 2);
             voff[j] = (uint32_t)(((int64_t)row * vsn + 8 * ch) * 2);
@@ -96,121 +100,125 @@ struct Stage {
         const auto kr = make_rsrc(kbase + (int64_t)kt0 * ksn, rows_bytes(kt0, N, ksn, D, kBK));
         const auto vr = make_rsrc(vbase + (int64_t)kt0 * vsn, rows_bytes(kt0, N, vsn, D, kBK));
 #pragma unroll
-        for (int j = 0; j < C::KCH; ++j) k[j] = buf_load16(kr, koff[j], 0);
+        for (int j = 0; j < KCH; ++j) k[j] = buf_load16(kr, koff[j], 0);
 #pragma unroll
-        for (int j = 0; j < C::KCH; ++j) v[j] = buf_load16(vr, voff[j], 0);
+        for (int j = 0; j < KCH; ++j) v[j] = buf_load16(vr, voff[j], 0);
     }
     __device__ void store(uint16_t* buf) const {
 #pragma unroll
-        for (int j = 0; j < C::KCH; ++j) *reinterpret_cast<u32x4*>(buf + klds[j]) = k[j];
+        for (int j = 0; j < KCH; ++j) *reinterpret_cast<u32x4*>(buf + klds[j]) = k[j];
 #pragma unroll
-        for (int j = 0; j < C::KCH; ++j) *reinterpret_cast<u32x4*>(buf + vlds[j]) = v[j];
+        for (int j = 0; j < KCH; ++j) *reinterpret_cast<u32x4*>(buf + vlds[j]) = v[j];
     }
 };
 
-// One 64-key step for one wave: scores for QB query blocks, masks (diagonal or tail tiles
-// only), online softmax update, P.V. `masked[qb]` is uniform across the wave.
-template <int D, int QB, bool CAUSAL>
-__device__ __forceinline__ void tile_step(const uint16_t* buf, const bf16x8 (&qf)[QB][Cfg<D>::KSTEPS],
-                                          f32x16 (&o)[QB][Cfg<D>::CB], float (&m_run)[QB], float (&l_part)[QB],
-                                          const bool (&masked)[QB], int kt0, int qw0, int N, float c, bool cpos,
-                                          int i, int hf) {
+// Per-wave state of 32 query rows.
+template <int D>
+struct Rows {
     using C = Cfg<D>;
-    f32x16 s[QB][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        s[qb][0] = f32x16{};
-        s[qb][1] = f32x16{};
-    }
-    // S^T = K Q^T. Row i of each 32-key block; the two blocks' chains alternate.
+    bf16x8 qf[C::KSTEPS];   // Q rows as B operands (column = query, k-group = half)
+    f32x16 o[C::CB];        // O^T accumulators
+    float m_run, l_part;    // running max (exp2 domain) and this lane's partial row sum
+    f32x16 s[2];            // scores of the current 64-key step (two 32-key blocks)
+    bf16x8 pb[2][2];        // probabilities of the current step as bf16 B operands
+};
+
+// S^T = K Q^T for one 64-key step. Row i of each 32-key block; the two blocks' chains alternate.
+template <int D>
+__device__ __forceinline__ void scores(const uint16_t* buf, Rows<D>& w, int i, int hf) {
+    using C = Cfg<D>;
+    w.s[0] = f32x16{};
+    w.s[1] = f32x16{};
     const uint16_t* kr = buf + i * C::KS + 8 * hf;
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+    for (int ks = 0; ks < C::KSTEPS; ++ks)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + 32 * kb * C::KS + 16 * ks);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(a, qf[qb][ks], s[qb][kb]);
-        }
-    }
+        for (int kb = 0; kb < 2; ++kb)
+            w.s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kr + 32 * kb * C::KS + 16 * ks), w.qf[ks], w.s[kb]);
+}
 
-    bf16x8 pb[QB][2][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = qw0 + 32 * qb + i;
-        // In masked tiles the scores are scaled here and masked keys (past the sequence end,
-        // or after the query under causal masking) become -inf; the exponent below then uses
-        // a unit multiplier. Elsewhere the scale is folded into the exponent's FMA.
-        float ce = c;
-        if (masked[qb]) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kt0 + 32 * kb + acc_row(r, hf);
-                    const bool ok = key < N && (!CAUSAL || key <= qrow);
-                    s[qb][kb][r] = ok ? s[qb][kb][r] * c : kNegInf;
-                }
-            ce = 1.0f;
-        }
-        float mt;
-        if (masked[qb] || cpos) {
-            mt = fmaxf(s[qb][0][0], s[qb][1][0]);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[qb][kb][r]);
-            mt = pair_max(mt);
-        } else {   // negative scale: the largest scaled score comes from the smallest raw one
-            mt = fminf(s[qb][0][0], s[qb][1][0]);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 1; r < 16; ++r) mt = fminf(mt, s[qb][kb][r]);
-            mt = pair_min(mt);
-        }
-        mt *= ce;
-
-        // Raise the running max only when the tile would push a probability above 2^8.
-        const bool need = mt > m_run[qb] + kRescaleSlack;
-        if (__any(need)) {
-            const float m_new = need ? mt : m_run[qb];
-            const float alpha = need ? fast_exp2(m_run[qb] - m_new) : 1.0f;
-            m_run[qb] = m_new;
-            l_part[qb] *= alpha;
-#pragma unroll
-            for (int cb = 0; cb < C::CB; ++cb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[qb][cb][r] *= alpha;
-        }
-        const float m_use = (m_run[qb] == kNegInf) ? 0.0f : m_run[qb];
-
-        // The row sum is taken in fp32 over the unrounded probabilities (the LSE contract
-        // needs it); P is rounded to bf16 only as the MFMA operand.
-        float psum = 0.0f;
+// Online softmax update for one step: mask (diagonal or tail tiles only), tile max, lazy
+// rescale, probabilities, fp32 row sum, bf16 operands. `masked` is uniform across the wave.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void softmax(Rows<D>& w, bool masked, int kt0, int qrow, int N, float c, bool cpos,
+                                        int hf) {
+    using C = Cfg<D>;
+    // In masked tiles the scores are scaled here and masked keys (past the sequence end,
+    // or after the query under causal masking) become -inf; the exponent below then uses
+    // a unit multiplier. Elsewhere the scale is folded into the exponent's FMA.
+    float ce = c;
+    if (masked) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(fmaf(s[qb][kb][r], ce, -m_use));
-                s[qb][kb][r] = p;
-                psum += p;
+                const int key = kt0 + 32 * kb + acc_row(r, hf);
+                const bool ok = key < N && (!CAUSAL || key <= qrow);
+                w.s[kb][r] = ok ? w.s[kb][r] * c : kNegInf;
             }
-        l_part[qb] += psum;
+        ce = 1.0f;
+    }
+    float mt;
+    if (masked || cpos) {
+        mt = fmaxf(w.s[0][0], w.s[1][0]);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
-                pb[qb][kb][st] = pack8(s[qb][kb][8 * st + 0], s[qb][kb][8 * st + 1], s[qb][kb][8 * st + 2],
-                                       s[qb][kb][8 * st + 3], s[qb][kb][8 * st + 4], s[qb][kb][8 * st + 5],
-                                       s[qb][kb][8 * st + 6], s[qb][kb][8 * st + 7]);
+            for (int r = 1; r < 16; ++r) mt = fmaxf(mt, w.s[kb][r]);
+        mt = pair_max(mt);
+    } else {   // negative scale: the largest scaled score comes from the smallest raw one
+        mt = fminf(w.s[0][0], w.s[1][0]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mt = fminf(mt, w.s[kb][r]);
+        mt = pair_min(mt);
     }
+    mt *= ce;
 
-    // O^T += V^T P^T. B element e of k-step st in half hf is key 16*st + 8*(e/4) + 4*hf + e%4
-    // of the 32-key block (the accumulator row order). The A operand (V^T: row = head-dim
-    // column, k = key) comes from the row-major V tile through two transposing reads: lane j
-    // of each 16-lane group addresses V[key0 + j/4][col0 + 4*(j%4)] and receives the 4 keys
-    // of column col0 + j.
+    // Raise the running max only when the tile would push a probability above 2^8.
+    const bool need = mt > w.m_run + kRescaleSlack;
+    if (__any(need)) {
+        const float m_new = need ? mt : w.m_run;
+        const float alpha = need ? fast_exp2(w.m_run - m_new) : 1.0f;
+        w.m_run = m_new;
+        w.l_part *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) w.o[cb][r] *= alpha;
+    }
+    const float m_use = (w.m_run == kNegInf) ? 0.0f : w.m_run;
+
+    // The row sum is taken in fp32 over the unrounded probabilities (the LSE needs it);
+    // P is rounded to bf16 only as the MFMA operand.
+    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four partial sums: short dependency chains
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pr = fast_exp2(fmaf(w.s[kb][r], ce, -m_use));
+            w.s[kb][r] = pr;
+            ps[r & 3] += pr;
+        }
+    w.l_part += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+            w.pb[kb][st] = pack8(w.s[kb][8 * st + 0], w.s[kb][8 * st + 1], w.s[kb][8 * st + 2],
+                                 w.s[kb][8 * st + 3], w.s[kb][8 * st + 4], w.s[kb][8 * st + 5],
+                                 w.s[kb][8 * st + 6], w.s[kb][8 * st + 7]);
+}
+
+// O^T += V^T P^T. B element e of k-step st in half hf is key 16*st + 8*(e/4) + 4*hf + e%4 of
+// the 32-key block (the accumulator row order). The A operand (V^T: row = head-dim column,
+// k = key) comes from the row-major V tile through two transposing reads: lane j of each
+// 16-lane group addresses V[key0 + j/4][col0 + 4*(j%4)] and receives the 4 keys of column
+// col0 + j.
+template <int D>
+__device__ __forceinline__ void pv(const uint16_t* buf, Rows<D>& w, int i, int hf) {
+    using C = Cfg<D>;
     const int g16 = (i >> 4) & 1, j16 = i & 15;
     const uint16_t* vr = buf + C::KEL + (4 * hf + (j16 >> 2)) * C::VS + 16 * g16 + 4 * (j16 & 3);
 #pragma unroll
@@ -223,24 +231,140 @@ __device__ __forceinline__ void tile_step(const uint16_t* buf, const bf16x8 (&qf
                 const uint16_t* p0 = vr + (32 * kb + 16 * st) * C::VS + 32 * cb;
                 const u32x2 lo = lds_read_tr4(p0);
                 const u32x2 hi = lds_read_tr4(p0 + 8 * C::VS);
-                u32x4 w;
-                w[0] = lo[0]; w[1] = lo[1]; w[2] = hi[0]; w[3] = hi[1];
-                a[kb][st] = as_bf16x8(w);
+                u32x4 x;
+                x[0] = lo[0]; x[1] = lo[1]; x[2] = hi[0]; x[3] = hi[1];
+                a[kb][st] = as_bf16x8(x);
             }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) o[qb][cb] = mfma32(a[kb][st], pb[qb][kb][st], o[qb][cb]);
+            for (int st = 0; st < 2; ++st) w.o[cb] = mfma32(a[kb][st], w.pb[kb][st], w.o[cb]);
     }
 }
 
-template <int D, int QB, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_kernel(Params p) {
+template <int D>
+__device__ __forceinline__ void load_q(Rows<D>& w, const uint16_t* qp, int64_t qsn, int qrow, int N, int hf) {
     using C = Cfg<D>;
-    constexpr int BQ = 128 * QB;
-    static_assert(!SPARSE || QB == 1, "a sparse workgroup covers exactly one 128-row block");
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks)
+        w.qf[ks] = as_bf16x8(load16(qp + (int64_t)qrow * qsn + 16 * ks + 8 * hf, qrow < N));
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb) w.o[cb] = f32x16{};
+    w.m_run = kNegInf;
+    w.l_part = 0.0f;
+}
+
+// O = O^T / l as bf16; LSE = (m + log2 l) * ln 2.
+template <int D>
+__device__ __forceinline__ void epilogue(const Rows<D>& w, const Params& p, int b, int hh, int bh, int qrow,
+                                         int hf) {
+    using C = Cfg<D>;
+    const float l_tot = pair_sum(w.l_part);
+    const int N = p.N;
+    if (qrow >= N) return;
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    uint16_t* orow = p.o + b * p.osb + hh * p.osh + (int64_t)qrow * p.osn;
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bf16x4 val;
+            val[0] = (__bf16)(w.o[cb][4 * j + 0] * inv);
+            val[1] = (__bf16)(w.o[cb][4 * j + 1] * inv);
+            val[2] = (__bf16)(w.o[cb][4 * j + 2] * inv);
+            val[3] = (__bf16)(w.o[cb][4 * j + 3] * inv);
+            *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * j + 4 * hf) = val;
+        }
+    if (hf == 0) p.lse[(int64_t)bh * N + qrow] = l_tot > 0.0f ? (w.m_run + log2f(l_tot)) * kLn2 : kNegInf;
+}
+
+// ----------------------------------------------------------------------------- dense, ping-pong
+constexpr int kPPThreads = 512;   // 8 waves, two groups of four
+constexpr int kPPRows = 256;      // query rows per workgroup
+constexpr int kPPBufs = 3;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_kernel(Params p) {
+    using C = Cfg<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[kPPBufs * C::BUF];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, i = lane & 31;
+    const int role = wave >> 2;   // group 1 runs one phase behind group 0
+
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = logical / p.nqb;
+    int qblk = logical % p.nqb;
+    if (CAUSAL) qblk = p.nqb - 1 - qblk;   // longest query blocks first
+    const int b = bh / p.H, hh = bh % p.H;
+    const int N = p.N;
+
+    const uint16_t* kp = p.k + b * p.ksb + hh * p.ksh;
+    const uint16_t* vp = p.v + b * p.vsb + hh * p.vsh;
+
+    const int q0 = qblk * kPPRows;
+    const int qw0 = q0 + 32 * wave;
+    const int qrow = qw0 + i;
+    const int qlast = min(q0 + kPPRows - 1, N - 1);
+
+    Rows<D> w;
+    load_q<D>(w, p.q + b * p.qsb + hh * p.qsh, p.qsn, qrow, N, hf);
+
+    int T = (N + kBK - 1) / kBK;
+    if (CAUSAL) T = min(T, qlast / kBK + 1);
+    // Steps this wave takes part in: all of them, or under causal masking those whose first
+    // key is not past the wave's last row.
+    const int Tw = CAUSAL ? min(T, (qw0 + 31) / kBK + 1) : T;
+    const bool rows_valid = qw0 < N;
+    const float c = p.c;
+    const bool cpos = c >= 0.0f;
+
+    Stage<D, kPPThreads> st;
+    st.init(tid, p.ksn, p.vsn);
+    if (T > 0) {
+        st.load(kp, vp, p.ksn, p.vsn, 0, N);
+        st.store(smem);
+    }
+    // Settle every outstanding load (the Q fragments included) so that no wait on them is
+    // left inside the loop; then start the loads of step 1.
+    __builtin_amdgcn_s_waitcnt(0);
+    if (T > 1) st.load(kp, vp, p.ksn, p.vsn, kBK, N);
+    __syncthreads();
+
+    // Phase ph: group g works on local phase lp = ph - g. Even lp = 2t: P.V of step t-1 and
+    // S of step t (MFMA); odd lp = 2t+1: softmax of step t (VALU). At the start of even
+    // phase 2s the loaded step s+1 is stored into buffer (s+1) % 3, whose previous occupant,
+    // step s-2, was last read in phase 2s-1 (group 1's P.V); step s+1 is first read in phase
+    // 2s+2. Then the loads of step s+2 are issued.
+    for (int ph = 0; ph < 2 * T + 2; ++ph) {
+        if ((ph & 1) == 0) {
+            const int s = ph >> 1;
+            if (s + 1 < T) st.store(smem + ((s + 1) % kPPBufs) * C::BUF);
+            if (s + 2 < T) st.load(kp, vp, p.ksn, p.vsn, (s + 2) * kBK, N);
+        }
+        const int lp = ph - role;
+        if (lp >= 0 && rows_valid) {
+            const int t = lp >> 1;
+            if ((lp & 1) == 0) {
+                if (t >= 1 && t - 1 < Tw) pv<D>(smem + ((t - 1) % kPPBufs) * C::BUF, w, i, hf);
+                if (t < Tw) scores<D>(smem + (t % kPPBufs) * C::BUF, w, i, hf);
+            } else if (t < Tw) {
+                const int kt = t * kBK;
+                const bool masked = (kt + kBK > N) || (CAUSAL && kt + kBK - 1 > qw0);
+                softmax<D, CAUSAL>(w, masked, kt, qrow, N, c, cpos, hf);
+            }
+        }
+        __syncthreads();
+    }
+    epilogue<D>(w, p, b, hh, bh, qrow, hf);
+}
+
+// ----------------------------------------------------------------------------- sparse
+constexpr int kSpThreads = 256;   // 4 waves, one 128-row block
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
+    using C = Cfg<D>;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
 
     const int tid = threadIdx.x;
@@ -248,71 +372,43 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_kernel(Params p
 
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = logical / p.nqb;
-    int qblk = logical % p.nqb;
-    if (CAUSAL || SPARSE) qblk = p.nqb - 1 - qblk;   // longest query blocks first
+    const int qblk = p.nqb - 1 - logical % p.nqb;   // longest lists first
     const int b = bh / p.H, hh = bh % p.H;
     const int N = p.N;
 
-    const uint16_t* qp = p.q + b * p.qsb + hh * p.qsh;
     const uint16_t* kp = p.k + b * p.ksb + hh * p.ksh;
     const uint16_t* vp = p.v + b * p.vsb + hh * p.vsh;
 
-    const int q0 = qblk * BQ;
-    const int qw0 = q0 + 32 * QB * wave;
-    const int qlast = min(q0 + BQ - 1, N - 1);
+    const int q0 = qblk * kSparseBlock;
+    const int qw0 = q0 + 32 * wave;
+    const int qrow = qw0 + i;
+    const int qlast = min(q0 + kSparseBlock - 1, N - 1);
 
-    bf16x8 qf[QB][C::KSTEPS];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = qw0 + 32 * qb + i;
-#pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks)
-            qf[qb][ks] = as_bf16x8(load16(qp + (int64_t)qrow * p.qsn + 16 * ks + 8 * hf, qrow < N));
-    }
+    Rows<D> w;
+    load_q<D>(w, p.q + b * p.qsb + hh * p.qsh, p.qsn, qrow, N, hf);
 
-    // Pipeline steps. Dense: step t covers keys [64t, 64t+64). Sparse: step t covers half
-    // (t & 1) of the listed key block kv_indices[t >> 1].
-    int t_end;
-    int t = 0;
+    // Step t covers half (t & 1) of the listed key block kv_indices[t >> 1]. Offsets are
+    // clamped to [0, nnz]; out-of-range and (causal) above-diagonal entries are skipped.
     const int nkb = (N + kSparseBlock - 1) / kSparseBlock;
-    if constexpr (SPARSE) {
-        int64_t lo = p.kv_offsets[qblk], hi = p.kv_offsets[qblk + 1];
-        lo = lo < 0 ? 0 : (lo > p.nnz ? p.nnz : lo);
-        hi = hi < lo ? lo : (hi > p.nnz ? p.nnz : hi);
-        t = (int)(2 * lo);
-        t_end = (int)(2 * hi);
-    } else {
-        t_end = (N + kBK - 1) / kBK;
-        if (CAUSAL) t_end = min(t_end, qlast / kBK + 1);
-    }
+    int64_t lo = p.kv_offsets[qblk], hi = p.kv_offsets[qblk + 1];
+    lo = lo < 0 ? 0 : (lo > p.nnz ? p.nnz : lo);
+    hi = hi < lo ? lo : (hi > p.nnz ? p.nnz : hi);
+    int t = (int)(2 * lo);
+    const int t_end = (int)(2 * hi);
     auto step_key = [&](int tt) -> int {   // first key of step tt, or -1 to skip it
-        if constexpr (SPARSE) {
-            const int kblk = p.kv_indices[tt >> 1];
-            if (kblk < 0 || kblk >= nkb || (CAUSAL && kblk > qblk)) return -1;
-            const int kt0 = kblk * kSparseBlock + (tt & 1) * kBK;
-            if (kt0 >= N || (CAUSAL && kt0 > qlast)) return -1;
-            return kt0;
-        } else {
-            return tt * kBK;
-        }
+        const int kblk = p.kv_indices[tt >> 1];
+        if (kblk < 0 || kblk >= nkb || (CAUSAL && kblk > qblk)) return -1;
+        const int kt0 = kblk * kSparseBlock + (tt & 1) * kBK;
+        if (kt0 >= N || (CAUSAL && kt0 > qlast)) return -1;
+        return kt0;
     };
-
     int kt = -1;
     while (t < t_end && (kt = step_key(t)) < 0) ++t;
 
-    f32x16 o[QB][C::CB];
-    float m_run[QB], l_part[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-        for (int cb = 0; cb < C::CB; ++cb) o[qb][cb] = f32x16{};
-        m_run[qb] = kNegInf;
-        l_part[qb] = 0.0f;
-    }
     const float c = p.c;
     const bool cpos = c >= 0.0f;
 
-    Stage<D> st;
+    Stage<D, kSpThreads> st;
     st.init(tid, p.ksn, p.vsn);
     if (t < t_end) {
         st.load(kp, vp, p.ksn, p.vsn, kt, N);
@@ -331,70 +427,39 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void fwd_kernel(Params p
         if (has_next) st.load(kp, vp, p.ksn, p.vsn, ktn, N);
 
         const uint16_t* buf = smem + cur * C::BUF;
-        bool active = false;
-        bool masked[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const int qs = qw0 + 32 * qb;
-            active |= qs < N && (!CAUSAL || kt <= qs + 31);
-            masked[qb] = (kt + kBK > N) || (CAUSAL && kt + kBK - 1 > qs);
+        if (qw0 < N && (!CAUSAL || kt <= qw0 + 31)) {
+            const bool masked = (kt + kBK > N) || (CAUSAL && kt + kBK - 1 > qw0);
+            scores<D>(buf, w, i, hf);
+            softmax<D, CAUSAL>(w, masked, kt, qrow, N, c, cpos, hf);
+            pv<D>(buf, w, i, hf);
         }
-        if (active) tile_step<D, QB, CAUSAL>(buf, qf, o, m_run, l_part, masked, kt, qw0, N, c, cpos, i, hf);
         if (has_next) st.store(smem + (cur ^ 1) * C::BUF);
         __syncthreads();
         cur ^= 1;
         t = tn;
         kt = ktn;
     }
-
-    // Epilogue: O = O^T / l as bf16; LSE = (m + log2 l) * ln 2.
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = qw0 + 32 * qb + i;
-        const float l_tot = pair_sum(l_part[qb]);
-        if (qrow < N) {
-            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-            uint16_t* orow = p.o + b * p.osb + hh * p.osh + (int64_t)qrow * p.osn;
-#pragma unroll
-            for (int cb = 0; cb < C::CB; ++cb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    bf16x4 val;
-                    val[0] = (__bf16)(o[qb][cb][4 * j + 0] * inv);
-                    val[1] = (__bf16)(o[qb][cb][4 * j + 1] * inv);
-                    val[2] = (__bf16)(o[qb][cb][4 * j + 2] * inv);
-                    val[3] = (__bf16)(o[qb][cb][4 * j + 3] * inv);
-                    *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * j + 4 * hf) = val;
-                }
-            if (hf == 0)
-                p.lse[(int64_t)bh * N + qrow] = l_tot > 0.0f ? (m_run[qb] + log2f(l_tot)) * kLn2 : kNegInf;
-        }
-    }
-}
-
-template <int D, int QB, bool CAUSAL, bool SPARSE>
-hipError_t launch(Params p, hipStream_t stream) {
-    p.nqb = (p.N + 128 * QB - 1) / (128 * QB);
-    const int64_t grid = (int64_t)p.B * p.H * p.nqb;
-    hipLaunchKernelGGL((fwd_kernel<D, QB, CAUSAL, SPARSE>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
-    return hipGetLastError();
-}
-
-// Rows per wave for the dense kernels: 1 -> 32, 2 -> 64 (FA_FWD_QB overrides, for tuning).
-int dense_qb() {
-    static const int qb = [] {
-        const char* e = std::getenv("FA_FWD_QB");
-        return (e && e[0] == '2') ? 2 : 1;
-    }();
-    return qb;
+    epilogue<D>(w, p, b, hh, bh, qrow, hf);
 }
 
 template <int D>
-hipError_t dispatch(const Params& p, bool causal, bool sparse, hipStream_t stream) {
-    if (sparse) return causal ? launch<D, 1, true, true>(p, stream) : launch<D, 1, false, true>(p, stream);
-    if (dense_qb() == 2)
-        return causal ? launch<D, 2, true, false>(p, stream) : launch<D, 2, false, false>(p, stream);
-    return causal ? launch<D, 1, true, false>(p, stream) : launch<D, 1, false, false>(p, stream);
+hipError_t dispatch(Params p, bool causal, bool sparse, hipStream_t stream) {
+    if (sparse) {
+        p.nqb = (p.N + kSparseBlock - 1) / kSparseBlock;
+        const int64_t grid = (int64_t)p.B * p.H * p.nqb;
+        if (causal)
+            hipLaunchKernelGGL((fwd_sparse_kernel<D, true>), dim3((unsigned)grid), dim3(kSpThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((fwd_sparse_kernel<D, false>), dim3((unsigned)grid), dim3(kSpThreads), 0, stream, p);
+        return hipGetLastError();
+    }
+    p.nqb = (p.N + kPPRows - 1) / kPPRows;
+    const int64_t grid = (int64_t)p.B * p.H * p.nqb;
+    if (causal)
+        hipLaunchKernelGGL((fwd_pingpong_kernel<D, true>), dim3((unsigned)grid), dim3(kPPThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fwd_pingpong_kernel<D, false>), dim3((unsigned)grid), dim3(kPPThreads), 0, stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace
