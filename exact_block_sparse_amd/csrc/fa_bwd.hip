@@ -13,13 +13,19 @@
 //    Bandwidth-bound: it reads O and dO once.
 // 2. dkdv_kernel: a workgroup owns 128 keys (32 per wave, one key per lane column) and
 //    walks the query tiles that can see them. K and V of the wave's keys stay in
-//    registers; Q and dO tiles are staged in LDS row-major (MFMA A operands of S and dP)
-//    and transposed (A operands of dK^T and dV^T). dK^T, dV^T accumulate in fp32.
+//    registers as MFMA B operands; S = Q K^T and dP = dO V^T read Q and dO rows from LDS;
+//    dV^T += dO^T P and dK^T += Q^T dS read the transposed operands straight from the
+//    row-major tiles with ds_read_b64_tr_b16. dK^T, dV^T accumulate in fp32.
 // 3. dq_kernel: a workgroup owns 128 query rows, as in the forward, and walks the key
-//    tiles: S^T = K Q^T and dP^T = V dO^T with Q and dO in registers, then
-//    dQ^T += K^T dS^T with K staged transposed in LDS.
+//    tiles: S^T = K Q^T and dP^T = V dO^T with Q and dO in registers, then dQ^T += K^T dS^T
+//    with K^T read transposed from the row-major K tile.
 // S and dP are thus computed twice (7 matrix products instead of 5) in exchange for no
 // atomics and bitwise-reproducible results.
+//
+// Every staged tile is written to LDS with plain 16-byte stores, once with a 272-byte row
+// stride (for 16-byte row reads) and, where a transposed operand is needed, once more with
+// a 320-byte stride (for the transposing reads): both access patterns are then free of
+// bank conflicts. Tiles are fetched with raw buffer loads that zero-fill rows past N.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -27,44 +33,49 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kStep = 64;   // rows per staged tile
 
-// Rows [r0, r0 + R) of a row-major [N, D] bf16 matrix (row stride sn elements), held in
-// registers as 4-row x 8-column blocks and written to LDS row-major (stride D + 8)
-// and/or transposed (stride R + 8). Rows at or past N read as zeros.
-template <int D, int R>
-struct TileStage {
-    static constexpr int CR = D / 8;
-    static constexpr int NBLK = (R / 4) * CR;
-    static constexpr int PER = (NBLK + kThreads - 1) / kThreads;
-    static constexpr int RS = D + 8;   // row-major LDS stride
-    static constexpr int TS = R + 8;   // transposed LDS stride
-    u32x4 r[PER][4];
+template <int D>
+struct BCfg {
+    static constexpr int RS = D + 8;            // row-read copy stride (elements)
+    static constexpr int TS = D + 32;           // transposed-read copy stride (elements)
+    static constexpr int RE = kStep * RS;
+    static constexpr int TE = kStep * TS;
+    static constexpr int CR = D / 8;            // 16-byte chunks per row
+    static constexpr int CH = kStep * CR / kThreads;
+    static constexpr int KSTEPS = D / 16;
+    static constexpr int CB = D / 32;
+};
 
-    __device__ __forceinline__ void load(const uint16_t* base, int64_t sn, int r0, int N, int tid) {
+// One 64-row tile of a [N, D] matrix (row stride sn elements) in registers: per thread CH
+// 16-byte chunks, loaded with a bounds-checked buffer load, stored to one or two LDS copies.
+template <int D>
+struct Tile {
+    using C = BCfg<D>;
+    u32x4 r[C::CH];
+    uint32_t goff[C::CH];
+    int roff[C::CH], toff[C::CH];
+
+    __device__ void init(int tid, int64_t sn) {
 #pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int blk = tid + p * kThreads;
-            const int cg = blk % CR, rg = blk / CR;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = r0 + 4 * rg + j;
-                r[p][j] = load16(base + (int64_t)row * sn + 8 * cg, blk < NBLK && row < N);
-            }
+        for (int j = 0; j < C::CH; ++j) {
+            const int id = tid + j * kThreads;
+            const int row = id / C::CR, ch = id % C::CR;
+            goff[j] = (uint32_t)(((int64_t)row * sn + 8 * ch) * 2);
+            roff[j] = row * C::RS + 8 * ch;
+            toff[j] = row * C::TS + 8 * ch;
         }
     }
-    __device__ __forceinline__ void store(uint16_t* rowmajor, uint16_t* transposed, int tid) const {
+    __device__ void load(const uint16_t* base, int64_t sn, int r0, int N) {
+        const auto rs = make_rsrc(base + (int64_t)r0 * sn, rows_bytes(r0, N, sn, D, kStep));
 #pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int blk = tid + p * kThreads;
-            if (blk >= NBLK) continue;
-            const int cg = blk % CR, rg = blk / CR;
-            if (rowmajor) {
+        for (int j = 0; j < C::CH; ++j) r[j] = buf_load16(rs, goff[j], 0);
+    }
+    __device__ void store(uint16_t* rowcopy, uint16_t* trcopy) const {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<u32x4*>(rowmajor + (4 * rg + j) * RS + 8 * cg) = r[p][j];
-            }
-            if (transposed)
-                store_transposed_4x8(transposed + (8 * cg) * TS + 4 * rg, TS, r[p][0], r[p][1], r[p][2], r[p][3]);
+        for (int j = 0; j < C::CH; ++j) {
+            if (rowcopy) *reinterpret_cast<u32x4*>(rowcopy + roff[j]) = r[j];
+            if (trcopy) *reinterpret_cast<u32x4*>(trcopy + toff[j]) = r[j];
         }
     }
 };
@@ -99,7 +110,6 @@ __global__ __launch_bounds__(kThreads) void pre_kernel(const uint16_t* o, int64_
 
 // ----------------------------------------------------------------------------- dK, dV
 constexpr int kKV_BK = 128;   // keys per workgroup (32 per wave)
-constexpr int kKV_BQ = 64;    // query rows per pipeline step
 
 struct KVParams {
     const uint16_t *q, *k, *v, *dout;
@@ -115,20 +125,20 @@ struct KVParams {
 
 template <int D>
 struct KVCfg {
-    using T = TileStage<D, kKV_BQ>;
-    static constexpr int RS = T::RS, TS = T::TS;
-    static constexpr int ROWEL = kKV_BQ * RS;          // a row-major tile
-    static constexpr int TREL = D * TS;                // a transposed tile
-    // stage layout: Q | Q^T | dO | dO^T | lse2[64] | delta[64] (floats at the end)
-    static constexpr int STAGE_U16 = 2 * ROWEL + 2 * TREL + 2 * kKV_BQ * 2;
+    using C = BCfg<D>;
+    // stage layout: Q rows | Q (transposed reads) | dO rows | dO (transposed reads) | lse2[64] | delta[64]
+    static constexpr int QR = 0, QT = C::RE, DR = C::RE + C::TE, DT = 2 * C::RE + C::TE;
+    static constexpr int STATS = 2 * C::RE + 2 * C::TE;
+    static constexpr int STAGE = STATS + 2 * kStep * 2;   // in uint16 units
+    static_assert((STATS * 2) % 16 == 0 && (STAGE * 2) % 16 == 0, "16-byte alignment");
 };
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
-    using C = KVCfg<D>;
-    using T = typename C::T;
-    constexpr int KSTEPS = D / 16, CB = D / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE_U16];
+    using C = BCfg<D>;
+    using L = KVCfg<D>;
+    constexpr int KSTEPS = C::KSTEPS, CB = C::CB;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::STAGE];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, i = lane & 31;
@@ -165,105 +175,107 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
         dv[cb] = f32x16{};
     }
 
-    const int nsteps = (N + kKV_BQ - 1) / kKV_BQ;
-    int t = CAUSAL ? k0 / kKV_BQ : 0;
+    const int nsteps = (N + kStep - 1) / kStep;
+    int t = CAUSAL ? k0 / kStep : 0;
     const float c = p.c;
 
-    T sq, sd;
-    float st_lse = 0.0f, st_del = 0.0f;
+    Tile<D> tq, td;
+    tq.init(tid, p.qsn);
+    td.init(tid, p.dsn);
+    float st_stat = 0.0f;
     auto load_step = [&](int tt) {
-        const int r0 = tt * kKV_BQ;
-        sq.load(qp, p.qsn, r0, N, tid);
-        sd.load(dp, p.dsn, r0, N, tid);
-        if (tid < kKV_BQ) {
+        const int r0 = tt * kStep;
+        tq.load(qp, p.qsn, r0, N);
+        td.load(dp, p.dsn, r0, N);
+        if (tid < kStep) {
             const int row = r0 + tid;
-            // Rows past N get LSE = +inf, so their recomputed probabilities are exactly 0.
+            // Rows past N get LSE = +inf, so their recomputed probabilities are exactly 0;
+            // so do rows that saw no key at all (LSE = -inf).
             float l = row < N ? lsep[row] : __builtin_inff();
-            if (l == -__builtin_inff()) l = __builtin_inff();   // a row that saw no key
-            st_lse = l * kLog2e;
-        } else if (tid < 2 * kKV_BQ) {
-            const int row = r0 + tid - kKV_BQ;
-            st_del = row < N ? delp[row] : 0.0f;
+            if (l == -__builtin_inff()) l = __builtin_inff();
+            st_stat = l * kLog2e;
+        } else if (tid < 2 * kStep) {
+            const int row = r0 + tid - kStep;
+            st_stat = row < N ? delp[row] : 0.0f;
         }
     };
     auto store_step = [&](uint16_t* s) {
-        sq.store(s, s + C::ROWEL, tid);
-        sd.store(s + C::ROWEL + C::TREL, s + 2 * C::ROWEL + C::TREL, tid);
-        float* f = reinterpret_cast<float*>(s + 2 * C::ROWEL + 2 * C::TREL);
-        if (tid < kKV_BQ) f[tid] = st_lse;
-        else if (tid < 2 * kKV_BQ) f[tid] = st_del;
+        tq.store(s + L::QR, s + L::QT);
+        td.store(s + L::DR, s + L::DT);
+        if (tid < 2 * kStep) reinterpret_cast<float*>(s + L::STATS)[tid] = st_stat;
     };
 
     if (t < nsteps) {
         load_step(t);
         store_step(smem);
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int cur = 0;
     for (; t < nsteps; ++t) {
         const bool has_next = t + 1 < nsteps;
         if (has_next) load_step(t + 1);
 
-        const uint16_t* s = smem + cur * C::STAGE_U16;
-        const uint16_t* sQ = s;
-        const uint16_t* sQT = s + C::ROWEL;
-        const uint16_t* sD = s + C::ROWEL + C::TREL;
-        const uint16_t* sDT = s + 2 * C::ROWEL + C::TREL;
-        const float* sL = reinterpret_cast<const float*>(s + 2 * C::ROWEL + 2 * C::TREL);
-        const float* sDel = sL + kKV_BQ;
-        const int qt0 = t * kKV_BQ;
-        const bool active = key - i < N && (!CAUSAL || qt0 + kKV_BQ - 1 >= kw0);
-        if (active) {
+        const uint16_t* s = smem + cur * L::STAGE;
+        const float* sL = reinterpret_cast<const float*>(s + L::STATS);
+        const float* sDel = sL + kStep;
+        const uint16_t* qt_base = tr_lane_base(s + L::QT, C::TS, lane);
+        const uint16_t* dt_base = tr_lane_base(s + L::DT, C::TS, lane);
+        const int qt0 = t * kStep;
+        if (kw0 < N && (!CAUSAL || qt0 + kStep - 1 >= kw0)) {
 #pragma unroll
-            for (int qb = 0; qb < kKV_BQ / 32; ++qb) {
+            for (int qb = 0; qb < kStep / 32; ++qb) {
                 if (CAUSAL && qt0 + 32 * qb + 31 < kw0) continue;   // every query before every key
-                // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys. A-operand
-                // row i holds query swz(i), so the accumulator hands out 8 consecutive queries
-                // per lane and k-step below.
+                // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys.
                 f32x16 sacc = {}, pacc = {};
-                const uint16_t* qr = sQ + (32 * qb + swz(i)) * C::RS + 8 * hf;
-                const uint16_t* dr = sD + (32 * qb + swz(i)) * C::RS + 8 * hf;
+                const uint16_t* qr = s + L::QR + (32 * qb + i) * C::RS + 8 * hf;
+                const uint16_t* dr = s + L::DR + (32 * qb + i) * C::RS + 8 * hf;
 #pragma unroll
                 for (int ks = 0; ks < KSTEPS; ++ks) {
                     sacc = mfma32(*reinterpret_cast<const bf16x8*>(qr + 16 * ks), kf[ks], sacc);
                     pacc = mfma32(*reinterpret_cast<const bf16x8*>(dr + 16 * ks), vf[ks], pacc);
                 }
+                // Element r of this lane is query 32*qb + 8*(r/4) + 4*hf + r%4.
                 const bool masked = CAUSAL && qt0 + 32 * qb < kw0 + 31;
+                float lq[16], dq[16];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + 32 * qb + 8 * g + 4 * hf);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(sDel + 32 * qb + 8 * g + 4 * hf);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        lq[4 * g + e] = l4[e];
+                        dq[4 * g + e] = d4[e];
+                    }
+                }
+                float pv[16], dsv[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float pe = fast_exp2(fmaf(sacc[r], c, -lq[r]));
+                    if (masked && key > qt0 + 32 * qb + acc_row(r, hf)) pe = 0.0f;
+                    pv[r] = pe;
+                    dsv[r] = pe * (pacc[r] - dq[r]);
+                }
                 bf16x8 pb[2], db[2];
 #pragma unroll
                 for (int st = 0; st < 2; ++st) {
-                    const int q8 = 32 * qb + 16 * st + 8 * hf;   // first of this lane's 8 queries
-                    const f32x4 l0 = *reinterpret_cast<const f32x4*>(sL + q8);
-                    const f32x4 l1 = *reinterpret_cast<const f32x4*>(sL + q8 + 4);
-                    const f32x4 d0 = *reinterpret_cast<const f32x4*>(sDel + q8);
-                    const f32x4 d1 = *reinterpret_cast<const f32x4*>(sDel + q8 + 4);
-                    float pv[8], dsv[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float lq = e < 4 ? l0[e] : l1[e - 4];
-                        const float dq = e < 4 ? d0[e] : d1[e - 4];
-                        float pe = fast_exp2(fmaf(sacc[8 * st + e], c, -lq));
-                        if (masked && key > qt0 + q8 + e) pe = 0.0f;
-                        pv[e] = pe;
-                        dsv[e] = pe * (pacc[8 * st + e] - dq);
-                    }
-                    pb[st] = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-                    db[st] = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+                    pb[st] = pack8(pv[8 * st], pv[8 * st + 1], pv[8 * st + 2], pv[8 * st + 3], pv[8 * st + 4],
+                                   pv[8 * st + 5], pv[8 * st + 6], pv[8 * st + 7]);
+                    db[st] = pack8(dsv[8 * st], dsv[8 * st + 1], dsv[8 * st + 2], dsv[8 * st + 3], dsv[8 * st + 4],
+                                   dsv[8 * st + 5], dsv[8 * st + 6], dsv[8 * st + 7]);
                 }
                 // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries.
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    const uint16_t* dtr = sDT + (32 * cb + i) * C::TS + 32 * qb + 8 * hf;
-                    const uint16_t* qtr = sQT + (32 * cb + i) * C::TS + 32 * qb + 8 * hf;
+                for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
                     for (int st = 0; st < 2; ++st) {
-                        dv[cb] = mfma32(*reinterpret_cast<const bf16x8*>(dtr + 16 * st), pb[st], dv[cb]);
-                        dk[cb] = mfma32(*reinterpret_cast<const bf16x8*>(qtr + 16 * st), db[st], dk[cb]);
+                        const int off = (32 * qb + 16 * st) * C::TS + 32 * cb;
+                        dv[cb] = mfma32(read_tr_operand(dt_base, off, C::TS), pb[st], dv[cb]);
+                        dk[cb] = mfma32(read_tr_operand(qt_base, off, C::TS), db[st], dk[cb]);
                     }
-                }
             }
         }
-        if (has_next) store_step(smem + (cur ^ 1) * C::STAGE_U16);
+        if (has_next) store_step(smem + (cur ^ 1) * L::STAGE);
         __syncthreads();
         cur ^= 1;
     }
@@ -290,7 +302,6 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
 
 // ----------------------------------------------------------------------------- dQ
 constexpr int kQ_BQ = 128;   // query rows per workgroup (32 per wave)
-constexpr int kQ_BK = 64;    // keys per pipeline step
 
 struct QParams {
     const uint16_t *q, *k, *v, *dout;
@@ -305,20 +316,20 @@ struct QParams {
 
 template <int D>
 struct QCfg {
-    using T = TileStage<D, kQ_BK>;
-    static constexpr int RS = T::RS, TS = T::TS;
-    static constexpr int ROWEL = kQ_BK * RS;
-    static constexpr int TREL = D * TS;
-    // stage layout: K | K^T | V
-    static constexpr int STAGE_U16 = 2 * ROWEL + TREL;
+    using C = BCfg<D>;
+    // one stage: K rows | K (transposed reads) | V rows
+    static constexpr int KR = 0, KT = C::RE, VR = C::RE + C::TE;
+    static constexpr int STAGE = 2 * C::RE + C::TE;
 };
 
+// Single LDS stage (two workgroups fit on a CU): the next tile is loaded into registers
+// during the current step and written after a barrier.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void dq_kernel(QParams p) {
-    using C = QCfg<D>;
-    using T = typename C::T;
-    constexpr int KSTEPS = D / 16, CB = D / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE_U16];
+__global__ __launch_bounds__(kThreads, 2) void dq_kernel(QParams p) {
+    using C = BCfg<D>;
+    using L = QCfg<D>;
+    constexpr int KSTEPS = C::KSTEPS, CB = C::CB;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[L::STAGE];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, i = lane & 31;
@@ -358,77 +369,67 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(QParams p) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) dq[cb] = f32x16{};
 
-    int nsteps = (N + kQ_BK - 1) / kQ_BK;
-    if (CAUSAL) nsteps = min(nsteps, qlast / kQ_BK + 1);
+    int nsteps = (N + kStep - 1) / kStep;
+    if (CAUSAL) nsteps = min(nsteps, qlast / kStep + 1);
     const float c = p.c;
+    const uint16_t* kt_base = tr_lane_base(smem + L::KT, C::TS, lane);
 
-    T sk, sv;
+    Tile<D> tk, tv;
+    tk.init(tid, p.ksn);
+    tv.init(tid, p.vsn);
     if (nsteps > 0) {
-        sk.load(kp, p.ksn, 0, N, tid);
-        sv.load(vp, p.vsn, 0, N, tid);
-        sk.store(smem, smem + C::ROWEL, tid);
-        sv.store(smem + C::ROWEL + C::TREL, nullptr, tid);
+        tk.load(kp, p.ksn, 0, N);
+        tv.load(vp, p.vsn, 0, N);
     }
-    __syncthreads();
-    int cur = 0;
+    __builtin_amdgcn_s_waitcnt(0);
     for (int t = 0; t < nsteps; ++t) {
-        const bool has_next = t + 1 < nsteps;
-        if (has_next) {
-            sk.load(kp, p.ksn, (t + 1) * kQ_BK, N, tid);
-            sv.load(vp, p.vsn, (t + 1) * kQ_BK, N, tid);
+        tk.store(smem + L::KR, smem + L::KT);
+        tv.store(smem + L::VR, nullptr);
+        __syncthreads();
+        if (t + 1 < nsteps) {
+            tk.load(kp, p.ksn, (t + 1) * kStep, N);
+            tv.load(vp, p.vsn, (t + 1) * kStep, N);
         }
-        const uint16_t* s = smem + cur * C::STAGE_U16;
-        const uint16_t* sK = s;
-        const uint16_t* sKT = s + C::ROWEL;
-        const uint16_t* sV = s + C::ROWEL + C::TREL;
-        const int kt = t * kQ_BK;
-        const bool active = qw0 < N && (!CAUSAL || kt <= qw0 + 31);
-        if (active) {
-            const bool masked = (kt + kQ_BK > N) || (CAUSAL && kt + kQ_BK - 1 > qw0);
+        const int kt = t * kStep;
+        if (qw0 < N && (!CAUSAL || kt <= qw0 + 31)) {
+            const bool masked = (kt + kStep > N) || (CAUSAL && kt + kStep - 1 > qw0);
             bf16x8 db[2][2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 f32x16 sacc = {}, pacc = {};
-                const uint16_t* kr = sK + (32 * kb + swz(i)) * C::RS + 8 * hf;
-                const uint16_t* vr = sV + (32 * kb + swz(i)) * C::RS + 8 * hf;
+                const uint16_t* kr = smem + L::KR + (32 * kb + i) * C::RS + 8 * hf;
+                const uint16_t* vr = smem + L::VR + (32 * kb + i) * C::RS + 8 * hf;
 #pragma unroll
                 for (int ks = 0; ks < KSTEPS; ++ks) {
                     sacc = mfma32(*reinterpret_cast<const bf16x8*>(kr + 16 * ks), qf[ks], sacc);
                     pacc = mfma32(*reinterpret_cast<const bf16x8*>(vr + 16 * ks), df[ks], pacc);
                 }
+                float dsv[16];
 #pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    float dsv[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        float pe = fast_exp2(fmaf(sacc[8 * st + e], c, -lse2));
-                        if (masked) {
-                            const int kk = kt + 32 * kb + 16 * st + 8 * hf + e;
-                            if (kk >= N || (CAUSAL && kk > qrow)) pe = 0.0f;
-                        }
-                        dsv[e] = pe * (pacc[8 * st + e] - dlt);
+                for (int r = 0; r < 16; ++r) {
+                    float pe = fast_exp2(fmaf(sacc[r], c, -lse2));
+                    if (masked) {
+                        const int kk = kt + 32 * kb + acc_row(r, hf);
+                        if (kk >= N || (CAUSAL && kk > qrow)) pe = 0.0f;
                     }
-                    db[kb][st] = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+                    dsv[r] = pe * (pacc[r] - dlt);
                 }
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+                    db[kb][st] = pack8(dsv[8 * st], dsv[8 * st + 1], dsv[8 * st + 2], dsv[8 * st + 3],
+                                       dsv[8 * st + 4], dsv[8 * st + 5], dsv[8 * st + 6], dsv[8 * st + 7]);
             }
             // dQ^T += K^T dS^T
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-                const uint16_t* ktr = sKT + (32 * cb + i) * C::TS + 8 * hf;
+            for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int st = 0; st < 2; ++st)
-                        dq[cb] = mfma32(*reinterpret_cast<const bf16x8*>(ktr + 32 * kb + 16 * st), db[kb][st], dq[cb]);
-            }
-        }
-        if (has_next) {
-            uint16_t* n = smem + (cur ^ 1) * C::STAGE_U16;
-            sk.store(n, n + C::ROWEL, tid);
-            sv.store(n + C::ROWEL + C::TREL, nullptr, tid);
+                        dq[cb] = mfma32(read_tr_operand(kt_base, (32 * kb + 16 * st) * C::TS + 32 * cb, C::TS),
+                                        db[kb][st], dq[cb]);
         }
         __syncthreads();
-        cur ^= 1;
     }
 
     if (qrow < N) {

@@ -124,4 +124,22 @@ __device__ __forceinline__ u32x2 lds_read_tr4(const uint16_t* p) {
     return __builtin_bit_cast(u32x2, v);
 }
 
+// A operand of a 32x32x16 MFMA holding M^T (row = column of M, k = 8 rows of M), read from
+// a row-major bf16 tile M with two transposing reads. `lane_base` is the per-lane address
+//   M + (4*hf + j/4) * stride + 16*g + 4*(j%4)      (j = lane % 16, g = (lane / 16) % 2),
+// and `off` = r0 * stride + c0 selects rows r0 .. r0 + 15 and columns c0 .. c0 + 31: element
+// e of the lane with row c (= lane % 32) is M[r0 + 8*(e/4) + 4*hf + e%4][c0 + c], the order
+// in which a 32x32 accumulator hands its rows to a B operand.
+__device__ __forceinline__ bf16x8 read_tr_operand(const uint16_t* lane_base, int off, int stride) {
+    const u32x2 lo = lds_read_tr4(lane_base + off);
+    const u32x2 hi = lds_read_tr4(lane_base + off + 8 * stride);
+    u32x4 x;
+    x[0] = lo[0]; x[1] = lo[1]; x[2] = hi[0]; x[3] = hi[1];
+    return as_bf16x8(x);
+}
+__device__ __forceinline__ const uint16_t* tr_lane_base(const uint16_t* tile, int stride, int lane) {
+    const int hf = lane >> 5, g = (lane >> 4) & 1, j = lane & 15;
+    return tile + (4 * hf + (j >> 2)) * stride + 16 * g + 4 * (j & 3);
+}
+
 }  // namespace fa
