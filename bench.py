@@ -31,6 +31,25 @@ HBM_PEAK_GBS = 8000.0
 HEADLINE = "causal_h32_n32k"
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_fwd_causal_h32_n32k.md")
+FWD_SOURCE = os.path.join(ROOT, "exact_block_sparse_amd", "csrc", "fa_fwd.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline kernel from the committed rocprofv3 summary
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the kernel source has changed
+    since the counters were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        d = json.loads(blob)
+        cur = hashlib.sha256(open(FWD_SOURCE, "rb").read()).hexdigest()[:16]
+    except (OSError, IndexError, ValueError):
+        return None
+    return int(d["traffic_bytes"]) if d.get("source_sha256_16") == cur else None
+
+
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
@@ -268,8 +287,9 @@ def main():
                    "causal": w.causal, "scale": w.scale, "seed": w.seed, "sigma": w.sigma},
         "pct_of_peak": round(100 * achieved / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "fwd_kernel<128, causal>", "per_launch_flop": head["flops"],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(), "algorithmic_bytes": head["bytes"],
+                     "kernel": "fwd_pingpong_kernel<128, causal>", "per_launch_flop": head["flops"],
                      "avg_launch_ms": round(t["mean_ms"], 4)},
         "cpu_baseline": cpu,
         "workloads": others,
