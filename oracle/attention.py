@@ -30,8 +30,23 @@ and, by the chain rule through S = scale * Q K^T (the page's sketch leaves the s
 out of the dQ and dK lines), dQ_i = scale * sum_j dS_ij k_j, dK_j += scale * dS_ij q_i,
 dV_j += P_ij dO_i. The backward uses this module's own fp64 forward.
 
+Grouped key/value heads (page 1, FAQ on grouped-query and multi-query attention: the
+tiling is unchanged, the K and V heads are replicated over fewer copies): K and V may
+have H_kv heads with H divisible by H_kv; query head h reads key/value head
+h // (H / H_kv), so consecutive query heads share one K/V head (the replication reading
+taken here; H_kv = 1 is multi-query attention). In the backward a K/V head's gradient is
+the sum of the gradients its query heads send it, as the chain rule gives for a shared
+input.
+
+Variable-length batches (page 1, production notes on request batching and the FAQ on the
+varlen entry point: padding tokens are masked out of every softmax): sequences of
+different lengths are packed one after another along the token axis, sequence b being
+rows cu_seqlens[b] .. cu_seqlens[b+1] - 1; each sequence attends only to itself, exactly
+as if it were run alone. ``attention_forward_varlen`` and ``attention_backward_varlen``
+do just that, sequence by sequence.
+
 All arithmetic is float64. Inputs may be bf16 torch tensors or numpy arrays; they are
-upcast exactly. Arrays are logical (B, H, N, d).
+upcast exactly. Arrays are logical (B, H, N, d); K and V are (B, H_kv, N, d).
 """
 from __future__ import annotations
 
@@ -121,15 +136,23 @@ def forward_row(q, K, V, keys, scale):
     return p @ V[keys], m + math.log(l)
 
 
+def kv_head(h: int, H: int, H_kv: int) -> int:
+    """The key/value head query head ``h`` reads: h // (H / H_kv)."""
+    if H_kv <= 0 or H % H_kv:
+        raise ValueError(f"H={H} is not a multiple of H_kv={H_kv}")
+    return h // (H // H_kv)
+
+
 def attention_forward(Q, K, V, *, causal: bool, scale: float, sparse: dict | None = None,
                       rows=None, heads=None):
-    """O (B,H,N,d) and LSE (B,H,N) in fp64.
+    """O (B,H,N,d) and LSE (B,H,N) in fp64. K and V may have H_kv heads (grouped).
 
     ``rows``: optional iterable of query rows to compute (others are left NaN).
     ``heads``: optional iterable of (b, h) pairs to compute (others are left NaN).
     """
     Q, K, V = _f64(Q), _f64(K), _f64(V)
     B, H, N, d = Q.shape
+    H_kv = K.shape[1]
     scale = float(scale)
     O = np.full((B, H, N, V.shape[-1]), np.nan)
     LSE = np.full((B, H, N), np.nan)
@@ -137,7 +160,8 @@ def attention_forward(Q, K, V, *, causal: bool, scale: float, sparse: dict | Non
     head_list = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
     ks = KeySets(N, causal, sparse)
     for (b, h) in head_list:
-        Kb, Vb, Qb = K[b, h], V[b, h], Q[b, h]
+        g = kv_head(h, H, H_kv)
+        Kb, Vb, Qb = K[b, g], V[b, g], Q[b, h]
         for i in row_list:
             O[b, h, i], LSE[b, h, i] = forward_row(Qb[i], Kb, Vb, ks.keys(i), scale)
     return O, LSE
@@ -145,21 +169,31 @@ def attention_forward(Q, K, V, *, causal: bool, scale: float, sparse: dict | Non
 
 def attention_backward(Q, K, V, dO, *, causal: bool, scale: float, sparse: dict | None = None,
                        heads=None, return_forward: bool = False):
-    """dQ, dK, dV (B,H,N,d) in fp64, from the oracle's own forward."""
+    """dQ (B,H,N,d), dK and dV (B,H_kv,N,d) in fp64, from the oracle's own forward.
+
+    With grouped heads, dK and dV of a K/V head sum over the query heads that read it.
+    ``heads`` limits the query heads computed; K/V heads none of them reads stay NaN.
+    """
     Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
     B, H, N, d = Q.shape
+    H_kv = K.shape[1]
     scale = float(scale)
     dQ = np.full(Q.shape, np.nan)
     dK = np.full(K.shape, np.nan)
     dV = np.full(V.shape, np.nan)
-    O = np.full(V.shape, np.nan)
+    O = np.full(Q.shape[:3] + (V.shape[-1],), np.nan)
     LSE = np.full((B, H, N), np.nan)
     head_list = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    for (b, h) in head_list:
+        g = kv_head(h, H, H_kv)
+        dK[b, g] = 0.0
+        dV[b, g] = 0.0
     ks = KeySets(N, causal, sparse)
     for (b, h) in head_list:
-        Qb, Kb, Vb, dOb = Q[b, h], K[b, h], V[b, h], dO[b, h]
-        dKb = np.zeros_like(Kb)
-        dVb = np.zeros_like(Vb)
+        g = kv_head(h, H, H_kv)
+        Qb, Kb, Vb, dOb = Q[b, h], K[b, g], V[b, g], dO[b, h]
+        dKb = dK[b, g]   # views: the group's query heads add into the same K/V head
+        dVb = dV[b, g]
         for i in range(N):
             keys = ks.keys(i)
             s = row_scores(Qb[i], Kb, keys, scale)
@@ -177,8 +211,6 @@ def attention_backward(Q, K, V, dO, *, causal: bool, scale: float, sparse: dict 
             dQ[b, h, i] = scale * (ds @ Kb[keys])   # dQ_i = scale * sum_j dS_ij k_j
             dKb[keys] += scale * np.outer(ds, Qb[i])  # dK_j += scale * dS_ij q_i
             dVb[keys] += np.outer(p, dOb[i])          # dV_j += P_ij dO_i
-        dK[b, h] = dKb
-        dV[b, h] = dVb
     if return_forward:
         return dQ, dK, dV, O, LSE
     return dQ, dK, dV
@@ -186,7 +218,8 @@ def attention_backward(Q, K, V, dO, *, causal: bool, scale: float, sparse: dict 
 
 def backward_rows_dq(Q, K, V, dO, *, causal, scale, sparse=None, b=0, h=0, rows=()):
     """dQ for selected query rows of one head (each row needs only its own keys)."""
-    Q, K, V, dO = _f64(Q[b, h]), _f64(K[b, h]), _f64(V[b, h]), _f64(dO[b, h])
+    g = kv_head(h, Q.shape[1], K.shape[1])
+    Q, K, V, dO = _f64(Q[b, h]), _f64(K[b, g]), _f64(V[b, g]), _f64(dO[b, h])
     N = Q.shape[0]
     ks = KeySets(N, causal, sparse)
     out = {}
@@ -201,3 +234,62 @@ def backward_rows_dq(Q, K, V, dO, *, causal, scale, sparse=None, b=0, h=0, rows=
         ds = p * (dp - float(p @ dp))
         out[int(i)] = scale * (ds @ K[keys])
     return out
+
+
+def _segments(cu_seqlens, total: int):
+    cu = np.asarray(cu_seqlens, dtype=np.int64).reshape(-1)
+    if cu.size < 1 or cu[0] != 0 or cu[-1] != total or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must start at 0, end at the token count and not decrease")
+    return [(int(cu[b]), int(cu[b + 1])) for b in range(cu.size - 1)]
+
+
+def attention_forward_varlen(Q, K, V, cu_seqlens, *, causal: bool, scale: float,
+                             sparse: dict | None = None, rows=None):
+    """Packed variable-length forward: Q (T,H,d), K and V (T,H_kv,d) -> O (T,H,d), LSE (H,T).
+
+    Sequence b is rows cu_seqlens[b] .. cu_seqlens[b+1]-1 and attends only to itself (causal
+    positions and block numbers count from its own first row). ``rows``: optional packed
+    row indices to compute (others left NaN).
+    """
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    T, H, d = Q.shape
+    O = np.full((T, H, V.shape[-1]), np.nan)
+    LSE = np.full((H, T), np.nan)
+    want = None if rows is None else set(int(r) for r in rows)
+    for (s, e) in _segments(cu_seqlens, T):
+        if e == s:
+            continue
+        local = None if want is None else [r - s for r in sorted(want) if s <= r < e]
+        if local is not None and not local:
+            continue
+        q = Q[s:e].transpose(1, 0, 2)[None]
+        k = K[s:e].transpose(1, 0, 2)[None]
+        v = V[s:e].transpose(1, 0, 2)[None]
+        o, lse = attention_forward(q, k, v, causal=causal, scale=scale, sparse=sparse, rows=local)
+        O[s:e] = o[0].transpose(1, 0, 2)
+        LSE[:, s:e] = lse[0]
+    return O, LSE
+
+
+def attention_backward_varlen(Q, K, V, dO, cu_seqlens, *, causal: bool, scale: float,
+                              sparse: dict | None = None, return_forward: bool = False):
+    """Packed variable-length backward: dQ (T,H,d), dK and dV (T,H_kv,d), per sequence."""
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    T, H, d = Q.shape
+    dQ, dK, dV = np.zeros(Q.shape), np.zeros(K.shape), np.zeros(V.shape)
+    O = np.zeros((T, H, V.shape[-1]))
+    LSE = np.full((H, T), -math.inf)
+    for (s, e) in _segments(cu_seqlens, T):
+        if e == s:
+            continue
+        tr = lambda x: x[s:e].transpose(1, 0, 2)[None]
+        dq, dk, dv, o, lse = attention_backward(tr(Q), tr(K), tr(V), tr(dO), causal=causal, scale=scale,
+                                                sparse=sparse, return_forward=True)
+        dQ[s:e] = dq[0].transpose(1, 0, 2)
+        dK[s:e] = dk[0].transpose(1, 0, 2)
+        dV[s:e] = dv[0].transpose(1, 0, 2)
+        O[s:e] = o[0].transpose(1, 0, 2)
+        LSE[:, s:e] = lse[0]
+    if return_forward:
+        return dQ, dK, dV, O, LSE
+    return dQ, dK, dV

@@ -74,3 +74,22 @@ def key_mask_from_lists(n: int, block: int, offsets, indices, causal: bool) -> n
     if causal:
         m &= np.tril(np.ones((n, n), dtype=bool))
     return m
+
+
+def transpose_lists(offsets, indices, n_blocks: int):
+    """The same pattern seen from the key side, in CSR form: for every K-block, the
+    ascending Q-blocks whose lists name it. The backward's dK/dV pass walks these
+    (page 3's FAQ on training: the backward reuses the forward's tiling and masking).
+    """
+    off = np.asarray(offsets, dtype=np.int64)
+    idx = np.asarray(indices, dtype=np.int64)
+    per_key: list[list[int]] = [[] for _ in range(n_blocks)]
+    for q in range(n_blocks):
+        for t in range(int(off[q]), int(off[q + 1])):
+            per_key[int(idx[t])].append(q)
+    t_off = [0]
+    t_idx: list[int] = []
+    for k in range(n_blocks):
+        t_idx.extend(sorted(per_key[k]))
+        t_off.append(len(t_idx))
+    return np.asarray(t_off, dtype=np.int32), np.asarray(t_idx, dtype=np.int32)
