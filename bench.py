@@ -3,7 +3,8 @@
 Headline (`value`): causal bf16 forward, B=1 H=32 N=32768 d=128 (the 32K x 128 case),
 one step = one fa_fwd call over inputs already resident in HBM. The other workloads
 (small dense head, 7B-like causal layer in (B,N,H,d), 128K block-sparse, causal
-backward) are timed in the same run and reported under "workloads".
+backward; grouped K/V heads, packed variable-length sequences, block-sparse backward)
+are timed in the same run and reported under "workloads".
 
 FLOP conventions: forward 4*B*H*N^2*d, halved for causal; backward 2.5x the forward
 (five matrix products against two); block-sparse: listed 128x128 tiles x 4*128*128*d
@@ -55,7 +56,9 @@ def log(msg: str) -> None:
 
 
 def fwd_flops(w) -> float:
-    f = 4.0 * w.B * w.H * w.N * w.N * w.d
+    """4*H*n^2*d per sequence of n rows (halved for causal), summed over the batch."""
+    sq = sum(n * n for n in w.seqlens) if w.packed else w.B * w.N * w.N
+    f = 4.0 * w.H * sq * w.d
     return f / 2 if w.causal else f
 
 
@@ -78,12 +81,15 @@ def sparse_flops(w, offsets, indices) -> tuple[float, float]:
 
 
 def algorithmic_bytes(w, direction: str, nnz: int = 0) -> int:
-    t = w.B * w.H * w.N * w.d * 2
-    lse = w.B * w.H * w.N * 4
-    if direction == "bwd":
-        return 8 * t + lse                      # q k v o do read, dq dk dv written, lse read
-    extra = 0 if direction == "fwd" else (len_off(w) + nnz) * 4
-    return 4 * t + lse + extra                  # q k v read, o written, lse written
+    rows = w.total                              # B*N, or the packed row count
+    tq = rows * w.H * w.d * 2                   # one bf16 tensor with the query heads
+    tk = rows * w.hkv * w.d * 2                 # one bf16 tensor with the K/V heads
+    lse = rows * w.H * 4
+    lists = 0 if not w.sparse else (len_off(w) + nnz) * 4
+    if direction in ("bwd", "sparse_bwd"):
+        # q k v o do read, dq dk dv written, lse read (+ both list forms)
+        return 4 * tq + 4 * tk + lse + (2 * lists if w.sparse else 0)
+    return 2 * tq + 2 * tk + lse + lists        # q k v read, o written, lse written
 
 
 def len_off(w) -> int:
@@ -121,10 +127,31 @@ def prepare(fa, W, torch, key):
     x = W.make_inputs(w)
     dev = {n: t.to("cuda") for n, t in x.items()}
     info = dict(workload=w, x=x, dev=dev)
+    # grouped heads and packed sequences go through the general entry points
+    general = w.packed or w.hkv != w.H
+    kw = dict(causal=w.causal, scale=w.scale)
+    if w.packed:
+        kw.update(cu_seqlens=torch.from_numpy(w.cu_seqlens()).to("cuda"), max_seqlen=w.N)
     if w.direction == "fwd":
-        info["fn"] = lambda: fa.fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale)
+        if general:
+            info["fn"] = lambda: fa.attn_fwd(dev["q"], dev["k"], dev["v"], **kw)
+        else:
+            info["fn"] = lambda: fa.fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale)
         info["flops"] = fwd_flops(w)
         info["bytes"] = algorithmic_bytes(w, "fwd")
+    elif w.direction == "sparse_bwd":
+        nb = (w.N + w.sparse["block"] - 1) // w.sparse["block"]
+        off, idx = fa.make_block_lists(nb, w.sparse["window"], w.sparse["stride"], causal=w.causal,
+                                       rule=w.sparse["rule"])
+        t_off, t_idx = fa.transpose_block_lists(off, idx, nb)
+        lists = dict(kv_offsets=torch.from_numpy(off).to("cuda"), kv_indices=torch.from_numpy(idx).to("cuda"))
+        tlists = dict(q_offsets=torch.from_numpy(t_off).to("cuda"), q_indices=torch.from_numpy(t_idx).to("cuda"))
+        o, lse = fa.attn_fwd(dev["q"], dev["k"], dev["v"], **kw, **lists)
+        info["fn"] = lambda: fa.attn_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], **kw, **lists, **tlists)
+        fl, fl_exact = sparse_flops(w, off, idx)
+        info["flops"], info["flops_exact"] = 2.5 * fl, 2.5 * fl_exact
+        info["tiles_per_head"] = int(off[-1])
+        info["bytes"] = algorithmic_bytes(w, "sparse_bwd", len(idx))
     elif w.direction == "sparse_fwd":
         nb = (w.N + w.sparse["block"] - 1) // w.sparse["block"]
         off, idx = fa.make_block_lists(nb, w.sparse["window"], w.sparse["stride"], causal=w.causal,
@@ -136,6 +163,11 @@ def prepare(fa, W, torch, key):
         info["flops"], info["flops_exact"] = sparse_flops(w, off, idx)
         info["tiles_per_head"] = int(off[-1])
         info["bytes"] = algorithmic_bytes(w, "sparse_fwd", len(idx))
+    elif general:
+        o, lse = fa.attn_fwd(dev["q"], dev["k"], dev["v"], **kw)
+        info["fn"] = lambda: fa.attn_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], **kw)
+        info["flops"] = 2.5 * fwd_flops(w)
+        info["bytes"] = algorithmic_bytes(w, "bwd")
     else:
         o, lse = fa.fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale)
         info["fn"] = lambda: fa.bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], causal=w.causal,

@@ -10,10 +10,14 @@ no CPU or eager fallback: a missing library raises at import, a bad argument rai
     o, lse = sparse_fwd(q, k, v, offsets, indices)       # Flash-MSA block lists (CSR, int32)
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)
     offsets, indices = make_block_lists(n_blocks, window=8, stride=16)
+    o, lse = attn_fwd(q, k, v, causal=True)              # k, v may have fewer heads (GQA/MQA)
+    o, lse = attn_fwd(q, k, v, cu_seqlens=cu)            # packed [total, H, d] sequences
+    dq, dk, dv = attn_bwd(q, k, v, o, lse, do, kv_offsets=off, kv_indices=idx)   # sparse backward
 """
-from ._lib import EXPORTS, FA_STATUS, LIB_PATH, FaError, Strides, lib
-from .api import (bwd, bwd_workspace_bytes, check_block_lists, fwd, make_block_lists, sparse_fwd,
-                  status_str)
+from ._lib import EXPORTS, FA_STATUS, LIB_PATH, AttnDesc, FaError, Strides, lib
+from .api import (attn_bwd, attn_bwd_workspace_bytes, attn_fwd, bwd, bwd_workspace_bytes, check_block_lists, fwd,
+                  make_block_lists, sparse_fwd, status_str, transpose_block_lists)
 
-__all__ = ["fwd", "sparse_fwd", "bwd", "bwd_workspace_bytes", "make_block_lists", "check_block_lists",
-           "status_str", "FaError", "Strides", "lib", "LIB_PATH", "EXPORTS", "FA_STATUS"]
+__all__ = ["fwd", "sparse_fwd", "bwd", "bwd_workspace_bytes", "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes",
+           "make_block_lists", "check_block_lists", "transpose_block_lists", "status_str", "FaError", "Strides",
+           "AttnDesc", "lib", "LIB_PATH", "EXPORTS", "FA_STATUS"]

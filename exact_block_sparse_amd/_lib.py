@@ -14,13 +14,23 @@ FA_STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 4: "FA_ERR_LAYOUT",
     5: "FA_ERR_LIST", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP", 8: "FA_ERR_ARG", 9: "FA_ERR_CAPACITY",
 }
-EXPORTS = ("fa_fwd", "fa_sparse_fwd", "fa_bwd_workspace_bytes", "fa_bwd", "fa_make_block_lists",
+EXPORTS = ("fa_fwd", "fa_sparse_fwd", "fa_bwd_workspace_bytes", "fa_bwd", "fa_attn_fwd",
+           "fa_attn_bwd_workspace_bytes", "fa_attn_bwd", "fa_transpose_block_lists", "fa_make_block_lists",
            "fa_check_block_lists", "fa_status_str", "fa_last_error")
 
 
 class Strides(ctypes.Structure):
     """fa_strides: element strides (b, h, n) of a logical [B, H, N, d] tensor."""
     _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("n", ctypes.c_int64)]
+
+
+class AttnDesc(ctypes.Structure):
+    """fa_attn_desc: problem description of fa_attn_fwd / fa_attn_bwd (field order as in fa.h)."""
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("H_kv", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("d", ctypes.c_int64), ("causal", ctypes.c_int), ("scale", ctypes.c_float),
+                ("cu_seqlens", ctypes.c_void_p), ("total", ctypes.c_int64), ("block_size", ctypes.c_int64),
+                ("kv_offsets", ctypes.c_void_p), ("kv_indices", ctypes.c_void_p), ("nnz", ctypes.c_int64),
+                ("q_offsets", ctypes.c_void_p), ("q_indices", ctypes.c_void_p)]
 
 
 class FaError(RuntimeError):
@@ -47,6 +57,16 @@ def _load() -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                            S, S, S, S, S, S, S, S, i32, f32, vp, ctypes.c_size_t, vp]
     lib.fa_bwd.restype = i32
+    D = ctypes.POINTER(AttnDesc)
+    sz = ctypes.c_size_t
+    lib.fa_attn_fwd.argtypes = [D, vp, S, vp, S, vp, S, vp, S, vp, vp]
+    lib.fa_attn_fwd.restype = i32
+    lib.fa_attn_bwd_workspace_bytes.argtypes = [D]
+    lib.fa_attn_bwd_workspace_bytes.restype = sz
+    lib.fa_attn_bwd.argtypes = [D, vp, S, vp, S, vp, S, vp, S, vp, S, vp, vp, S, vp, S, vp, S, vp, sz, vp]
+    lib.fa_attn_bwd.restype = i32
+    lib.fa_transpose_block_lists.argtypes = [i64, pi32, pi32, i64, pi32, pi32]
+    lib.fa_transpose_block_lists.restype = i32
     lib.fa_make_block_lists.argtypes = [i64, ctypes.c_int32, ctypes.c_int32, i32, i32, pi32, pi32, i64,
                                         ctypes.POINTER(ctypes.c_int64)]
     lib.fa_make_block_lists.restype = i32

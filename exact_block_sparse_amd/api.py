@@ -13,7 +13,7 @@ import math
 import numpy as np
 import torch
 
-from ._lib import FaError, Strides, check, lib
+from ._lib import AttnDesc, FaError, Strides, check, lib
 
 BLOCK = 128
 
@@ -170,3 +170,169 @@ def check_block_lists(offsets, indices, n_blocks: int, causal: bool = True) -> N
     st = lib.fa_check_block_lists(off.ctypes.data_as(p32), idx.ctypes.data_as(p32) if idx.size else None,
                                   n_blocks, idx.size, int(bool(causal)))
     check(st, "fa_check_block_lists")
+
+
+# ----------------------------------------------------------------------------- general calls
+def transpose_block_lists(offsets, indices, n_blocks: int):
+    """Key-side form of host CSR block lists via ``fa_transpose_block_lists`` (host int32)."""
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    idx = np.ascontiguousarray(indices, dtype=np.int32)
+    if off.size != n_blocks + 1:
+        raise FaError(5, f"offsets has {off.size} entries, {n_blocks + 1} expected", "fa_transpose_block_lists")
+    t_off = np.zeros(n_blocks + 1, dtype=np.int32)
+    t_idx = np.zeros(max(idx.size, 1), dtype=np.int32)
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    st = lib.fa_transpose_block_lists(n_blocks, off.ctypes.data_as(p32), idx.ctypes.data_as(p32) if idx.size else None,
+                                      idx.size, t_off.ctypes.data_as(p32), t_idx.ctypes.data_as(p32))
+    check(st, "fa_transpose_block_lists")
+    return t_off, t_idx[: idx.size]
+
+
+def _packed_strides(t: torch.Tensor) -> Strides:
+    if t.dim() != 3:
+        raise ValueError(f"expected a packed 3-d [total, heads, d] tensor, got shape {tuple(t.shape)}")
+    if t.stride(2) != 1 and t.shape[2] > 1:
+        raise ValueError("the head dimension must be contiguous (stride 1)")
+    return Strides(0, t.stride(1), t.stride(0))
+
+
+def _check_group(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, packed: bool) -> None:
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"expected bfloat16 tensors, got {t.dtype}")
+        if t.device.type != "cuda" or t.device != q.device:
+            raise ValueError("tensors must be on one GPU device")
+    hd = 1
+    if tuple(k.shape) != tuple(v.shape):
+        raise ValueError(f"k and v shapes differ: {tuple(k.shape)} vs {tuple(v.shape)}")
+    same = [i for i in range(q.dim()) if i != hd]
+    if any(q.shape[i] != k.shape[i] for i in same):
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} differ outside the head axis")
+
+
+def _desc(B, H, H_kv, N, d, causal, scale, cu=None, total=0, lists=None) -> AttnDesc:
+    x = AttnDesc()
+    x.B, x.H, x.H_kv, x.N, x.d = B, H, H_kv, N, d
+    x.causal, x.scale = int(bool(causal)), float(scale)
+    x.cu_seqlens = cu.data_ptr() if cu is not None else None
+    x.total = int(total)
+    if lists is not None:
+        x.block_size = lists["block"]
+        x.kv_offsets, x.kv_indices = lists["off"].data_ptr(), lists["idx"].data_ptr()
+        x.nnz = lists["nnz"]
+        if "t_off" in lists:
+            x.q_offsets, x.q_indices = lists["t_off"].data_ptr(), lists["t_idx"].data_ptr()
+    return x
+
+
+def _seq_args(q: torch.Tensor, cu_seqlens, max_seqlen):
+    """(packed, B, N, total, cu device tensor or None)."""
+    if cu_seqlens is None:
+        B, _, N, _ = q.shape
+        return False, B, N, 0, None
+    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.device.type == "cuda":
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise TypeError("cu_seqlens must be a 1-d int32 tensor")
+        if max_seqlen is None:
+            raise ValueError("max_seqlen is required with device cu_seqlens")
+        cu = cu_seqlens.contiguous()
+    else:
+        host = np.asarray(cu_seqlens.cpu() if isinstance(cu_seqlens, torch.Tensor) else cu_seqlens, dtype=np.int64)
+        if host.ndim != 1 or host.size < 1 or host[0] != 0 or np.any(np.diff(host) < 0) or host[-1] > q.shape[0]:
+            raise ValueError("cu_seqlens must start at 0, not decrease and end within the packed rows")
+        if max_seqlen is None:
+            max_seqlen = int(np.max(np.diff(host))) if host.size > 1 else 0
+        cu = torch.from_numpy(host.astype(np.int32)).to(q.device)
+    return True, int(cu.numel()) - 1, int(max_seqlen), int(q.shape[0]), cu
+
+
+def _device_lists(kv_offsets, kv_indices, q_offsets, q_indices, n_blocks, causal, block_size, device, backward):
+    """Device copies of the query-side (and, for the backward, key-side) block lists."""
+    on_device = isinstance(kv_offsets, torch.Tensor) and kv_offsets.device.type == "cuda"
+    nnz = int(kv_indices.numel()) if on_device else int(np.asarray(
+        kv_indices.cpu() if isinstance(kv_indices, torch.Tensor) else kv_indices).size)
+    off, idx = _lists_to_device(kv_offsets, kv_indices, n_blocks, causal, device)
+    lists = dict(block=int(block_size), off=off, idx=idx, nnz=nnz)
+    if backward:
+        if q_offsets is None:
+            if on_device:
+                raise ValueError("pass q_offsets/q_indices with device lists (see transpose_block_lists)")
+            host_off = np.asarray(kv_offsets.cpu() if isinstance(kv_offsets, torch.Tensor) else kv_offsets)
+            host_idx = np.asarray(kv_indices.cpu() if isinstance(kv_indices, torch.Tensor) else kv_indices)
+            q_offsets, q_indices = transpose_block_lists(host_off, host_idx, n_blocks)
+        t_off, t_idx = _lists_to_device(q_offsets, q_indices, n_blocks, False, device)
+        lists["t_off"], lists["t_idx"] = t_off, t_idx
+    return lists
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+             scale: float | None = None, cu_seqlens=None, max_seqlen: int | None = None,
+             kv_offsets=None, kv_indices=None, block_size: int = BLOCK,
+             out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """General forward through ``fa_attn_fwd``: grouped K/V heads, packed sequences, block lists.
+
+    Fixed length: q [B, H, N, d], k and v [B, H_kv, N, d]; returns O like q and LSE [B, H, N].
+    Packed (``cu_seqlens`` given, int32 [B+1], host or device): q [total, H, d], k and v
+    [total, H_kv, d]; returns O like q and LSE [H, total]. ``max_seqlen`` bounds every
+    sequence's length (computed from host offsets when omitted).
+    """
+    packed = cu_seqlens is not None
+    _check_group(q, k, v, packed)
+    d = q.shape[-1]
+    H, H_kv = (q.shape[1], k.shape[1])
+    pk, B, N, total, cu = _seq_args(q, cu_seqlens, max_seqlen)
+    lists = None
+    if kv_offsets is not None:
+        nb = (N + block_size - 1) // block_size
+        lists = _device_lists(kv_offsets, kv_indices, None, None, nb, causal, block_size, q.device, False)
+    o = _empty_like_layout(q) if (out is None and not pk) else (torch.empty_like(q) if out is None else out)
+    lshape = (H, total) if pk else (B, H, N)
+    l = torch.empty(lshape, dtype=torch.float32, device=q.device) if lse is None else lse
+    S = _packed_strides if pk else _strides
+    x = _desc(B, H, H_kv, N, d, causal, _scale(scale, d), cu, total, lists)
+    with torch.cuda.device(q.device):
+        st = lib.fa_attn_fwd(ctypes.byref(x), _ptr(q), S(q), _ptr(k), S(k), _ptr(v), S(v), _ptr(o), S(o), _ptr(l),
+                             _stream(q.device))
+    check(st, "fa_attn_fwd")
+    return o, l
+
+
+def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int, total: int | None = None) -> int:
+    x = _desc(B, H, H, N, d, False, 1.0)
+    if total is not None:
+        x.cu_seqlens = 1   # any non-NULL value selects the packed layout; it is not read
+        x.total = int(total)
+    return int(lib.fa_attn_bwd_workspace_bytes(ctypes.byref(x)))
+
+
+def attn_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None = None, cu_seqlens=None,
+             max_seqlen: int | None = None, kv_offsets=None, kv_indices=None, q_offsets=None, q_indices=None,
+             block_size: int = BLOCK, workspace=None):
+    """General backward through ``fa_attn_bwd``; returns (dQ like q, dK like k, dV like v).
+
+    Arguments as in ``attn_fwd``; ``o`` and ``lse`` are its outputs. With host block lists
+    the key-side lists are derived with ``transpose_block_lists`` when not given.
+    """
+    packed = cu_seqlens is not None
+    _check_group(q, k, v, packed)
+    d = q.shape[-1]
+    H, H_kv = q.shape[1], k.shape[1]
+    pk, B, N, total, cu = _seq_args(q, cu_seqlens, max_seqlen)
+    lists = None
+    if kv_offsets is not None:
+        nb = (N + block_size - 1) // block_size
+        lists = _device_lists(kv_offsets, kv_indices, q_offsets, q_indices, nb, causal, block_size, q.device, True)
+    if pk:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = _empty_like_layout(q), _empty_like_layout(k), _empty_like_layout(v)
+    S = _packed_strides if pk else _strides
+    x = _desc(B, H, H_kv, N, d, causal, _scale(scale, d), cu, total, lists)
+    need = int(lib.fa_attn_bwd_workspace_bytes(ctypes.byref(x)))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    with torch.cuda.device(q.device):
+        st = lib.fa_attn_bwd(ctypes.byref(x), _ptr(q), S(q), _ptr(k), S(k), _ptr(v), S(v), _ptr(o), S(o), _ptr(do),
+                             S(do), _ptr(lse), _ptr(dq), S(dq), _ptr(dk), S(dk), _ptr(dv), S(dv), _ptr(ws),
+                             ws.numel(), _stream(q.device))
+    check(st, "fa_attn_bwd")
+    return dq, dk, dv

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "fa_internal.h"
 
@@ -72,85 +73,117 @@ int launched(hipError_t e, const char* what) {
 
 fa::View view(const void* p, const fa_strides& s) { return fa::View{p, s.b, s.h, s.n}; }
 
-int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-               int64_t N, int64_t d, fa_strides sq, fa_strides sk, fa_strides sv, fa_strides so, int causal,
-               float scale, const int32_t* kv_offsets, const int32_t* kv_indices, int64_t nnz,
-               void* stream) {
-    int st = check_sizes(B, H, N, d);
+bool packed(const fa_attn_desc& d) { return d.cu_seqlens != nullptr; }
+bool empty_problem(const fa_attn_desc& d) {
+    return d.B == 0 || d.H == 0 || d.N == 0 || (packed(d) && d.total == 0);
+}
+
+// Sizes, head grouping, sequence layout, scale and block lists of a descriptor.
+int check_desc(const fa_attn_desc* dp, bool backward) {
+    if (!dp) return fail(FA_ERR_NULL, "desc is NULL");
+    const fa_attn_desc& d = *dp;
+    int st = check_sizes(d.B, d.H, d.N, d.d);
     if (st) return st;
-    if (!std::isfinite(scale)) return fail(FA_ERR_ARG, "scale is not finite");
-    if (B == 0 || H == 0 || N == 0) return ok();
-    if ((st = check_tensor("q", q, sq)) || (st = check_tensor("k", k, sk)) || (st = check_tensor("v", v, sv)) ||
-        (st = check_tensor("o", o, so)))
-        return st;
+    if (d.H_kv < 0 || d.H_kv > kMaxDim) return fail(FA_ERR_SHAPE, "bad H_kv %lld", (long long)d.H_kv);
+    if (d.H > 0 && (d.H_kv == 0 || d.H % d.H_kv != 0))
+        return fail(FA_ERR_SHAPE, "H=%lld is not a multiple of H_kv=%lld", (long long)d.H, (long long)d.H_kv);
+    if (packed(d) && (d.total < 0 || d.total > kMaxDim))
+        return fail(FA_ERR_SHAPE, "bad packed row count total=%lld", (long long)d.total);
+    if (packed(d) && d.total * d.H > kMaxDim)
+        return fail(FA_ERR_SHAPE, "H * total too large (%lld * %lld)", (long long)d.H, (long long)d.total);
+    if (!std::isfinite(d.scale)) return fail(FA_ERR_ARG, "scale is not finite");
+    if (!d.kv_offsets && (d.kv_indices || d.q_offsets || d.q_indices))
+        return fail(FA_ERR_NULL, "block lists given without kv_offsets");
+    if (d.kv_offsets) {
+        if (d.block_size != 128) return fail(FA_ERR_SHAPE, "block size %lld not supported (128)", (long long)d.block_size);
+        if (d.nnz < 0) return fail(FA_ERR_LIST, "negative nnz");
+        if (!d.kv_indices && d.nnz > 0) return fail(FA_ERR_NULL, "kv_indices is NULL");
+        if (backward) {
+            if (!d.q_offsets) return fail(FA_ERR_NULL, "q_offsets is NULL (key-side lists are needed for dK, dV)");
+            if (!d.q_indices && d.nnz > 0) return fail(FA_ERR_NULL, "q_indices is NULL");
+        }
+    }
+    return FA_OK;
+}
+
+fa::Layout layout(const fa_attn_desc& d) {
+    fa::Layout L;
+    L.B = (int)d.B; L.H = (int)d.H; L.Hkv = (int)d.H_kv; L.N = (int)d.N; L.d = (int)d.d;
+    L.cu = d.cu_seqlens;
+    L.total = packed(d) ? d.total : 0;
+    return L;
+}
+
+// With nnz == 0 the kernels read no index; any valid pointer stands in for a NULL one.
+const int32_t* or_other(const int32_t* p, const int32_t* other) { return p ? p : other; }
+
+int check_lse(const float* lse) {
     if (!lse) return fail(FA_ERR_NULL, "lse is NULL");
     if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(FA_ERR_LAYOUT, "lse is not 4-byte aligned");
-    if ((st = check_device())) return st;
-    fa::FwdArgs a;
-    a.q = view(q, sq);
-    a.k = view(k, sk);
-    a.v = view(v, sv);
-    a.o = o;
-    a.osb = so.b; a.osh = so.h; a.osn = so.n;
-    a.lse = lse;
-    a.B = (int)B; a.H = (int)H; a.N = (int)N; a.d = (int)d;
-    a.causal = causal != 0;
-    a.scale = scale;
-    a.kv_offsets = kv_offsets;
-    a.kv_indices = kv_indices;
-    a.nnz = nnz;
-    return launched(fa::launch_fwd(a, static_cast<hipStream_t>(stream)), "forward");
+    return FA_OK;
+}
+
+fa_attn_desc plain_desc(int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale) {
+    fa_attn_desc x;
+    std::memset(&x, 0, sizeof x);
+    x.B = B; x.H = H; x.H_kv = H; x.N = N; x.d = d;
+    x.causal = causal;
+    x.scale = scale;
+    return x;
 }
 
 }  // namespace
 
 extern "C" {
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
-           int64_t d, fa_strides sq, fa_strides sk, fa_strides sv, fa_strides so, int causal, float scale,
-           void* stream) {
-    return fwd_common(q, k, v, o, lse, B, H, N, d, sq, sk, sv, so, causal, scale, nullptr, nullptr, 0, stream);
-}
-
-int fa_sparse_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                  int64_t N, int64_t d, fa_strides sq, fa_strides sk, fa_strides sv, fa_strides so,
-                  int64_t block_size, const int32_t* kv_offsets, const int32_t* kv_indices, int64_t nnz,
-                  int causal, float scale, void* stream) {
-    if (block_size != 128) return fail(FA_ERR_SHAPE, "block size %lld not supported (128)", (long long)block_size);
-    if (nnz < 0) return fail(FA_ERR_LIST, "negative nnz");
-    int st = check_sizes(B, H, N, d);
+int fa_attn_fwd(const fa_attn_desc* desc, const void* q, fa_strides sq, const void* k, fa_strides sk, const void* v,
+                fa_strides sv, void* o, fa_strides so, float* lse, void* stream) {
+    int st = check_desc(desc, false);
     if (st) return st;
-    if (B == 0 || H == 0 || N == 0) return ok();
-    if (!kv_offsets) return fail(FA_ERR_NULL, "kv_offsets is NULL");
-    if (!kv_indices && nnz > 0) return fail(FA_ERR_NULL, "kv_indices is NULL");
-    // With nnz == 0 the kernels read no index; any valid pointer stands in for a NULL one.
-    return fwd_common(q, k, v, o, lse, B, H, N, d, sq, sk, sv, so, causal, scale, kv_offsets,
-                      kv_indices ? kv_indices : kv_offsets, nnz, stream);
+    const fa_attn_desc& d = *desc;
+    if (empty_problem(d)) return ok();
+    if ((st = check_tensor("q", q, sq)) || (st = check_tensor("k", k, sk)) || (st = check_tensor("v", v, sv)) ||
+        (st = check_tensor("o", o, so)) || (st = check_lse(lse)))
+        return st;
+    if ((st = check_device())) return st;
+    fa::FwdArgs a;
+    a.L = layout(d);
+    a.q = view(q, sq);
+    a.k = view(k, sk);
+    a.v = view(v, sv);
+    a.o = o;
+    a.osb = so.b; a.osh = so.h; a.osn = so.n;
+    a.lse = lse;
+    a.causal = d.causal != 0;
+    a.scale = d.scale;
+    a.kv_offsets = d.kv_offsets;
+    a.kv_indices = d.kv_offsets ? or_other(d.kv_indices, d.kv_offsets) : nullptr;
+    a.nnz = d.kv_offsets ? d.nnz : 0;
+    return launched(fa::launch_fwd(a, static_cast<hipStream_t>(stream)), "forward");
 }
 
-size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
-    (void)d;
-    if (B <= 0 || H <= 0 || N <= 0) return 0;
-    const size_t bytes = (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+size_t fa_attn_bwd_workspace_bytes(const fa_attn_desc* desc) {
+    if (!desc || desc->B <= 0 || desc->H <= 0 || desc->N <= 0) return 0;
+    const int64_t rows = packed(*desc) ? desc->total : desc->B * desc->N;
+    if (rows <= 0) return 0;
+    const size_t bytes = (size_t)desc->H * (size_t)rows * sizeof(float);
     return (bytes + 255) & ~(size_t)255;
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
-           void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, fa_strides sq, fa_strides sk,
-           fa_strides sv, fa_strides so, fa_strides sdo, fa_strides sdq, fa_strides sdk, fa_strides sdv, int causal,
-           float scale, void* workspace, size_t workspace_bytes, void* stream) {
-    int st = check_sizes(B, H, N, d);
+int fa_attn_bwd(const fa_attn_desc* desc, const void* q, fa_strides sq, const void* k, fa_strides sk, const void* v,
+                fa_strides sv, const void* o, fa_strides so, const void* dout, fa_strides sdo, const float* lse,
+                void* dq, fa_strides sdq, void* dk, fa_strides sdk, void* dv, fa_strides sdv, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    int st = check_desc(desc, true);
     if (st) return st;
-    if (!std::isfinite(scale)) return fail(FA_ERR_ARG, "scale is not finite");
-    if (B == 0 || H == 0 || N == 0) return ok();
+    const fa_attn_desc& d = *desc;
+    if (empty_problem(d)) return ok();
     if ((st = check_tensor("q", q, sq)) || (st = check_tensor("k", k, sk)) || (st = check_tensor("v", v, sv)) ||
         (st = check_tensor("o", o, so)) || (st = check_tensor("dout", dout, sdo)) ||
         (st = check_tensor("dq", dq, sdq)) || (st = check_tensor("dk", dk, sdk)) ||
-        (st = check_tensor("dv", dv, sdv)))
+        (st = check_tensor("dv", dv, sdv)) || (st = check_lse(lse)))
         return st;
-    if (!lse) return fail(FA_ERR_NULL, "lse is NULL");
-    if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(FA_ERR_LAYOUT, "lse is not 4-byte aligned");
-    const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
+    const size_t need = fa_attn_bwd_workspace_bytes(desc);
     if (!workspace) return fail(FA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
     if (workspace_bytes < need)
         return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
@@ -167,10 +200,72 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     a.dk = dk; a.dksb = sdk.b; a.dksh = sdk.h; a.dksn = sdk.n;
     a.dv = dv; a.dvsb = sdv.b; a.dvsh = sdv.h; a.dvsn = sdv.n;
     a.delta = static_cast<float*>(workspace);
-    a.B = (int)B; a.H = (int)H; a.N = (int)N; a.d = (int)d;
-    a.causal = causal != 0;
-    a.scale = scale;
+    a.L = layout(d);
+    a.causal = d.causal != 0;
+    a.scale = d.scale;
+    const bool sparse = d.kv_offsets != nullptr;
+    a.kv_offsets = sparse ? d.kv_offsets : nullptr;
+    a.kv_indices = sparse ? or_other(d.kv_indices, d.kv_offsets) : nullptr;
+    a.q_offsets = sparse ? d.q_offsets : nullptr;
+    a.q_indices = sparse ? or_other(d.q_indices, d.q_offsets) : nullptr;
+    a.nnz = sparse ? d.nnz : 0;
     return launched(fa::launch_bwd(a, static_cast<hipStream_t>(stream)), "backward");
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+           int64_t d, fa_strides sq, fa_strides sk, fa_strides sv, fa_strides so, int causal, float scale,
+           void* stream) {
+    const fa_attn_desc x = plain_desc(B, H, N, d, causal, scale);
+    return fa_attn_fwd(&x, q, sq, k, sk, v, sv, o, so, lse, stream);
+}
+
+int fa_sparse_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                  int64_t N, int64_t d, fa_strides sq, fa_strides sk, fa_strides sv, fa_strides so,
+                  int64_t block_size, const int32_t* kv_offsets, const int32_t* kv_indices, int64_t nnz,
+                  int causal, float scale, void* stream) {
+    if (block_size != 128) return fail(FA_ERR_SHAPE, "block size %lld not supported (128)", (long long)block_size);
+    if (nnz < 0) return fail(FA_ERR_LIST, "negative nnz");
+    int st = check_sizes(B, H, N, d);
+    if (st) return st;
+    if (B == 0 || H == 0 || N == 0) return ok();
+    if (!kv_offsets) return fail(FA_ERR_NULL, "kv_offsets is NULL");
+    fa_attn_desc x = plain_desc(B, H, N, d, causal, scale);
+    x.block_size = block_size;
+    x.kv_offsets = kv_offsets;
+    x.kv_indices = kv_indices;
+    x.nnz = nnz;
+    return fa_attn_fwd(&x, q, sq, k, sk, v, sv, o, so, lse, stream);
+}
+
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+    const fa_attn_desc x = plain_desc(B, H, N, d, 0, 1.0f);
+    return fa_attn_bwd_workspace_bytes(&x);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+           void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, fa_strides sq, fa_strides sk,
+           fa_strides sv, fa_strides so, fa_strides sdo, fa_strides sdq, fa_strides sdk, fa_strides sdv, int causal,
+           float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    const fa_attn_desc x = plain_desc(B, H, N, d, causal, scale);
+    return fa_attn_bwd(&x, q, sq, k, sk, v, sv, o, so, dout, sdo, lse, dq, sdq, dk, sdk, dv, sdv, workspace,
+                       workspace_bytes, stream);
+}
+
+int fa_transpose_block_lists(int64_t n_blocks, const int32_t* offsets, const int32_t* indices, int64_t nnz,
+                             int32_t* t_offsets, int32_t* t_indices) {
+    if (n_blocks < 0 || n_blocks > kMaxDim || nnz < 0) return fail(FA_ERR_LIST, "negative or too large sizes");
+    if (!offsets || !t_offsets || (nnz > 0 && (!indices || !t_indices))) return fail(FA_ERR_NULL, "NULL pointer");
+    int st = fa_check_block_lists(offsets, indices, n_blocks, nnz, 0);
+    if (st) return st;
+    // Counting sort by key block; walking the query blocks in ascending order leaves every
+    // key block's query blocks ascending.
+    std::vector<int64_t> fill((size_t)n_blocks + 1, 0);
+    for (int64_t t = 0; t < nnz; ++t) ++fill[(size_t)indices[t] + 1];
+    for (int64_t kb = 0; kb < n_blocks; ++kb) fill[(size_t)kb + 1] += fill[(size_t)kb];
+    for (int64_t kb = 0; kb <= n_blocks; ++kb) t_offsets[kb] = (int32_t)fill[(size_t)kb];
+    for (int64_t qb = 0; qb < n_blocks; ++qb)
+        for (int64_t t = offsets[qb]; t < offsets[qb + 1]; ++t) t_indices[fill[(size_t)indices[t]]++] = (int32_t)qb;
+    return ok();
 }
 
 int fa_make_block_lists(int64_t n_blocks, int32_t window, int32_t stride, int causal, int rule, int32_t* offsets,

@@ -118,7 +118,13 @@ struct KVParams {
     uint16_t *dk, *dv;
     int64_t qsb, qsh, qsn, ksb, ksh, ksn, vsb, vsh, vsn, dsb, dsh, dsn;
     int64_t dksb, dksh, dksn, dvsb, dvsh, dvsn;
-    int B, H, N, nkb;
+    int B, H, Hkv, N, nkb;
+    int G;                 // query heads per K/V head
+    const int32_t* cu;     // packed sequence offsets [B + 1], or nullptr
+    int64_t total;
+    const int32_t* q_offsets;   // key-side block lists (block-sparse mode), or nullptr
+    const int32_t* q_indices;
+    int64_t nnz;
     float c;       // scale * log2(e)
     float scale;
 };
@@ -143,24 +149,21 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, i = lane & 31;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = logical / p.nkb, kblk = logical % p.nkb;   // ascending: longest first under causal
-    const int b = bh / p.H, hh = bh % p.H;
-    const int N = p.N;
-
-    const uint16_t* qp = p.q + b * p.qsb + hh * p.qsh;
-    const uint16_t* dp = p.dout + b * p.dsb + hh * p.dsh;
-    const float* lsep = p.lse + (int64_t)bh * N;
-    const float* delp = p.delta + (int64_t)bh * N;
-
+    const int bhk = logical / p.nkb, kblk = logical % p.nkb;   // ascending: longest first under causal
+    const int b = bhk / p.Hkv, hk = bhk % p.Hkv;
+    const SeqSpan sp = seq_span(p.cu, p.total, b, p.N);
+    const int N = sp.len;
     const int k0 = kblk * kKV_BK;
+    if (k0 >= N) return;   // past the end of a shorter packed sequence (uniform per workgroup)
+
     const int kw0 = k0 + 32 * wave;
     const int key = kw0 + i;
 
     // K and V rows of this lane's key as B operands (column = key, k-group = half).
     bf16x8 kf[KSTEPS], vf[KSTEPS];
     {
-        const uint16_t* kr = p.k + b * p.ksb + hh * p.ksh + (int64_t)key * p.ksn + 8 * hf;
-        const uint16_t* vr = p.v + b * p.vsb + hh * p.vsh + (int64_t)key * p.vsn + 8 * hf;
+        const uint16_t* kr = p.k + seq_off(sp, b, hk, p.ksb, p.ksh, p.ksn) + (int64_t)key * p.ksn + 8 * hf;
+        const uint16_t* vr = p.v + seq_off(sp, b, hk, p.vsb, p.vsh, p.vsn) + (int64_t)key * p.vsn + 8 * hf;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
             kf[ks] = as_bf16x8(load16(kr + 16 * ks, key < N));
@@ -175,28 +178,56 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
         dv[cb] = f32x16{};
     }
 
+    // Steps: 64-row query tiles, for each of the G query heads that read this K/V head in
+    // turn. Dense: the tiles from the first one that can see these keys (causal) or from 0 to
+    // the end. Block-sparse: both halves of every query block the key-side list names for
+    // this key block; entries out of range (or, causal, above the diagonal) are skipped.
     const int nsteps = (N + kStep - 1) / kStep;
-    int t = CAUSAL ? k0 / kStep : 0;
+    const int t0 = CAUSAL ? k0 / kStep : 0;
+    int64_t lo = 0, hi = 0;
+    const bool sparse = p.q_offsets != nullptr;
+    if (sparse) {
+        lo = p.q_offsets[kblk];
+        hi = p.q_offsets[kblk + 1];
+        lo = lo < 0 ? 0 : (lo > p.nnz ? p.nnz : lo);
+        hi = hi < lo ? lo : (hi > p.nnz ? p.nnz : hi);
+    }
+    const int per = sparse ? (int)(2 * (hi - lo)) : nsteps - t0;   // steps per query head
+    const int n_all = per * p.G;
+    const int nqb = (N + kKV_BK - 1) / kKV_BK;
+    // First query row of step s (-1: skip) and its query head.
+    auto step_row = [&](int s, int& hq) -> int {
+        const int g = s / per, j = s - g * per;
+        hq = hk * p.G + g;
+        if (!sparse) return (t0 + j) * kStep;
+        const int qb = p.q_indices[lo + (j >> 1)];
+        if (qb < 0 || qb >= nqb || (CAUSAL && qb < kblk)) return -1;
+        const int r0 = qb * kKV_BK + (j & 1) * kStep;
+        return r0 < N ? r0 : -1;
+    };
     const float c = p.c;
 
     Tile<D> tq, td;
     tq.init(tid, p.qsn);
     td.init(tid, p.dsn);
     float st_stat = 0.0f;
-    auto load_step = [&](int tt) {
-        const int r0 = tt * kStep;
-        tq.load(qp, p.qsn, r0, N);
-        td.load(dp, p.dsn, r0, N);
+    auto load_step = [&](int s) {
+        int hq;
+        const int r0 = step_row(s, hq);
+        if (r0 < 0) return;
+        tq.load(p.q + seq_off(sp, b, hq, p.qsb, p.qsh, p.qsn), p.qsn, r0, N);
+        td.load(p.dout + seq_off(sp, b, hq, p.dsb, p.dsh, p.dsn), p.dsn, r0, N);
+        const int64_t so = seq_stat_off(sp, b, hq, p.H, p.N, p.total);
         if (tid < kStep) {
             const int row = r0 + tid;
             // Rows past N get LSE = +inf, so their recomputed probabilities are exactly 0;
             // so do rows that saw no key at all (LSE = -inf).
-            float l = row < N ? lsep[row] : __builtin_inff();
+            float l = row < N ? p.lse[so + row] : __builtin_inff();
             if (l == -__builtin_inff()) l = __builtin_inff();
             st_stat = l * kLog2e;
         } else if (tid < 2 * kStep) {
             const int row = r0 + tid - kStep;
-            st_stat = row < N ? delp[row] : 0.0f;
+            st_stat = row < N ? p.delta[so + row] : 0.0f;
         }
     };
     auto store_step = [&](uint16_t* s) {
@@ -205,15 +236,15 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
         if (tid < 2 * kStep) reinterpret_cast<float*>(s + L::STATS)[tid] = st_stat;
     };
 
-    if (t < nsteps) {
-        load_step(t);
+    if (n_all > 0) {
+        load_step(0);
         store_step(smem);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int cur = 0;
-    for (; t < nsteps; ++t) {
-        const bool has_next = t + 1 < nsteps;
+    for (int t = 0; t < n_all; ++t) {
+        const bool has_next = t + 1 < n_all;
         if (has_next) load_step(t + 1);
 
         const uint16_t* s = smem + cur * L::STAGE;
@@ -221,8 +252,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
         const float* sDel = sL + kStep;
         const uint16_t* qt_base = tr_lane_base(s + L::QT, C::TS, lane);
         const uint16_t* dt_base = tr_lane_base(s + L::DT, C::TS, lane);
-        const int qt0 = t * kStep;
-        if (kw0 < N && (!CAUSAL || qt0 + kStep - 1 >= kw0)) {
+        int hq_unused;
+        const int qt0 = step_row(t, hq_unused);
+        if (qt0 >= 0 && kw0 < N && (!CAUSAL || qt0 + kStep - 1 >= kw0)) {
 #pragma unroll
             for (int qb = 0; qb < kStep / 32; ++qb) {
                 if (CAUSAL && qt0 + 32 * qb + 31 < kw0) continue;   // every query before every key
@@ -281,8 +313,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
     }
 
     if (key < N) {
-        uint16_t* dkr = p.dk + b * p.dksb + hh * p.dksh + (int64_t)key * p.dksn;
-        uint16_t* dvr = p.dv + b * p.dvsb + hh * p.dvsh + (int64_t)key * p.dvsn;
+        uint16_t* dkr = p.dk + seq_off(sp, b, hk, p.dksb, p.dksh, p.dksn) + (int64_t)key * p.dksn;
+        uint16_t* dvr = p.dv + seq_off(sp, b, hk, p.dvsb, p.dvsh, p.dvsn) + (int64_t)key * p.dvsn;
         const float sc = p.scale;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
@@ -310,6 +342,12 @@ struct QParams {
     uint16_t* dq;
     int64_t qsb, qsh, qsn, ksb, ksh, ksn, vsb, vsh, vsn, dsb, dsh, dsn, dqsb, dqsh, dqsn;
     int B, H, N, nqb;
+    int G;
+    const int32_t* cu;
+    int64_t total;
+    const int32_t* kv_offsets;   // query-side block lists (block-sparse mode), or nullptr
+    const int32_t* kv_indices;
+    int64_t nnz;
     float c;
     float scale;
 };
@@ -338,39 +376,63 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(QParams p) {
     int qb = logical % p.nqb;
     if (CAUSAL) qb = p.nqb - 1 - qb;
     const int b = bh / p.H, hh = bh % p.H;
-    const int N = p.N;
-
-    const uint16_t* kp = p.k + b * p.ksb + hh * p.ksh;
-    const uint16_t* vp = p.v + b * p.vsb + hh * p.vsh;
+    const SeqSpan sp = seq_span(p.cu, p.total, b, p.N);
+    const int N = sp.len;
     const int q0 = qb * kQ_BQ;
+    if (q0 >= N) return;   // past the end of a shorter packed sequence (uniform per workgroup)
+
+    const int hk = hh / p.G;
+    const uint16_t* kp = p.k + seq_off(sp, b, hk, p.ksb, p.ksh, p.ksn);
+    const uint16_t* vp = p.v + seq_off(sp, b, hk, p.vsb, p.vsh, p.vsn);
     const int qw0 = q0 + 32 * wave;
     const int qrow = qw0 + i;
     const int qlast = min(q0 + kQ_BQ - 1, N - 1);
 
     bf16x8 qf[KSTEPS], df[KSTEPS];
     {
-        const uint16_t* qr = p.q + b * p.qsb + hh * p.qsh + (int64_t)qrow * p.qsn + 8 * hf;
-        const uint16_t* dr = p.dout + b * p.dsb + hh * p.dsh + (int64_t)qrow * p.dsn + 8 * hf;
+        const uint16_t* qr = p.q + seq_off(sp, b, hh, p.qsb, p.qsh, p.qsn) + (int64_t)qrow * p.qsn + 8 * hf;
+        const uint16_t* dr = p.dout + seq_off(sp, b, hh, p.dsb, p.dsh, p.dsn) + (int64_t)qrow * p.dsn + 8 * hf;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
             qf[ks] = as_bf16x8(load16(qr + 16 * ks, qrow < N));
             df[ks] = as_bf16x8(load16(dr + 16 * ks, qrow < N));
         }
     }
+    const int64_t so = seq_stat_off(sp, b, hh, p.H, p.N, p.total);
     float lse2 = 0.0f, dlt = 0.0f;
     if (qrow < N) {
-        float l = p.lse[(int64_t)bh * N + qrow];
+        float l = p.lse[so + qrow];
         if (l == -__builtin_inff()) l = __builtin_inff();
         lse2 = l * kLog2e;
-        dlt = p.delta[(int64_t)bh * N + qrow];
+        dlt = p.delta[so + qrow];
     }
 
     f32x16 dq[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) dq[cb] = f32x16{};
 
+    // Steps: 64-key tiles. Dense: from 0 to the end (causal: to the block's last row).
+    // Block-sparse: both halves of every key block listed for this query block; entries out
+    // of range (or, causal, above the diagonal) are skipped.
     int nsteps = (N + kStep - 1) / kStep;
     if (CAUSAL) nsteps = min(nsteps, qlast / kStep + 1);
+    const bool sparse = p.kv_offsets != nullptr;
+    int64_t lo = 0;
+    if (sparse) {
+        int64_t hi = p.kv_offsets[qb + 1];
+        lo = p.kv_offsets[qb];
+        lo = lo < 0 ? 0 : (lo > p.nnz ? p.nnz : lo);
+        hi = hi < lo ? lo : (hi > p.nnz ? p.nnz : hi);
+        nsteps = (int)(2 * (hi - lo));
+    }
+    const int nkb = (N + kQ_BQ - 1) / kQ_BQ;
+    auto step_key = [&](int t) -> int {   // first key of step t, or -1 to skip it
+        if (!sparse) return t * kStep;
+        const int kb = p.kv_indices[lo + (t >> 1)];
+        if (kb < 0 || kb >= nkb || (CAUSAL && kb > qb)) return -1;
+        const int kt0 = kb * kQ_BQ + (t & 1) * kStep;
+        return (kt0 < N && (!CAUSAL || kt0 <= qlast)) ? kt0 : -1;
+    };
     const float c = p.c;
     const uint16_t* kt_base = tr_lane_base(smem + L::KT, C::TS, lane);
 
@@ -378,8 +440,11 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(QParams p) {
     tk.init(tid, p.ksn);
     tv.init(tid, p.vsn);
     if (nsteps > 0) {
-        tk.load(kp, p.ksn, 0, N);
-        tv.load(vp, p.vsn, 0, N);
+        const int kt0 = step_key(0);
+        if (kt0 >= 0) {
+            tk.load(kp, p.ksn, kt0, N);
+            tv.load(vp, p.vsn, kt0, N);
+        }
     }
     __builtin_amdgcn_s_waitcnt(0);
     for (int t = 0; t < nsteps; ++t) {
@@ -387,11 +452,14 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(QParams p) {
         tv.store(smem + L::VR, nullptr);
         __syncthreads();
         if (t + 1 < nsteps) {
-            tk.load(kp, p.ksn, (t + 1) * kStep, N);
-            tv.load(vp, p.vsn, (t + 1) * kStep, N);
+            const int ktn = step_key(t + 1);
+            if (ktn >= 0) {
+                tk.load(kp, p.ksn, ktn, N);
+                tv.load(vp, p.vsn, ktn, N);
+            }
         }
-        const int kt = t * kStep;
-        if (qw0 < N && (!CAUSAL || kt <= qw0 + 31)) {
+        const int kt = step_key(t);
+        if (kt >= 0 && qw0 < N && (!CAUSAL || kt <= qw0 + 31)) {
             const bool masked = (kt + kStep > N) || (CAUSAL && kt + kStep - 1 > qw0);
             bf16x8 db[2][2];
 #pragma unroll
@@ -433,7 +501,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(QParams p) {
     }
 
     if (qrow < N) {
-        uint16_t* dqr = p.dq + b * p.dqsb + hh * p.dqsh + (int64_t)qrow * p.dqsn;
+        uint16_t* dqr = p.dq + seq_off(sp, b, hh, p.dqsb, p.dqsh, p.dqsn) + (int64_t)qrow * p.dqsn;
         const float sc = p.scale;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
@@ -449,14 +517,20 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(QParams p) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
-    const int64_t rows = (int64_t)a.B * a.H * a.N;
-    constexpr int RPB = kThreads / (D / 8);
+    const Layout& L = a.L;
     {
+        // D has the LSE's layout: [B, H, N], or [H, total] for packed sequences, which is the
+        // same computation over one sequence of `total` rows.
+        const bool packed = L.cu != nullptr;
+        const int Bp = packed ? 1 : L.B;
+        const int Np = packed ? (int)L.total : L.N;
+        const int64_t rows = (int64_t)Bp * L.H * Np;
+        constexpr int RPB = kThreads / (D / 8);
         const int64_t grid = (rows + RPB - 1) / RPB;
         hipLaunchKernelGGL((pre_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                           static_cast<const uint16_t*>(a.o.p), a.o.sb, a.o.sh, a.o.sn,
-                           static_cast<const uint16_t*>(a.dout.p), a.dout.sb, a.dout.sh, a.dout.sn, a.delta, a.H,
-                           a.N, rows);
+                           static_cast<const uint16_t*>(a.o.p), packed ? 0 : a.o.sb, a.o.sh, a.o.sn,
+                           static_cast<const uint16_t*>(a.dout.p), packed ? 0 : a.dout.sb, a.dout.sh, a.dout.sn,
+                           a.delta, L.H, Np, rows);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -477,11 +551,17 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
         p.dsb = a.dout.sb; p.dsh = a.dout.sh; p.dsn = a.dout.sn;
         p.dksb = a.dksb; p.dksh = a.dksh; p.dksn = a.dksn;
         p.dvsb = a.dvsb; p.dvsh = a.dvsh; p.dvsn = a.dvsn;
-        p.B = a.B; p.H = a.H; p.N = a.N;
-        p.nkb = (a.N + kKV_BK - 1) / kKV_BK;
+        p.B = L.B; p.H = L.H; p.Hkv = L.Hkv; p.N = L.N;
+        p.G = L.H / L.Hkv;
+        p.cu = L.cu;
+        p.total = L.total;
+        p.q_offsets = a.kv_offsets ? a.q_offsets : nullptr;
+        p.q_indices = a.q_indices;
+        p.nnz = a.nnz;
+        p.nkb = (L.N + kKV_BK - 1) / kKV_BK;
         p.c = c;
         p.scale = a.scale;
-        const int64_t grid = (int64_t)a.B * a.H * p.nkb;
+        const int64_t grid = (int64_t)L.B * L.Hkv * p.nkb;
         hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -500,11 +580,17 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
         p.vsb = a.v.sb; p.vsh = a.v.sh; p.vsn = a.v.sn;
         p.dsb = a.dout.sb; p.dsh = a.dout.sh; p.dsn = a.dout.sn;
         p.dqsb = a.dqsb; p.dqsh = a.dqsh; p.dqsn = a.dqsn;
-        p.B = a.B; p.H = a.H; p.N = a.N;
-        p.nqb = (a.N + kQ_BQ - 1) / kQ_BQ;
+        p.B = L.B; p.H = L.H; p.N = L.N;
+        p.G = L.H / L.Hkv;
+        p.cu = L.cu;
+        p.total = L.total;
+        p.kv_offsets = a.kv_offsets;
+        p.kv_indices = a.kv_indices;
+        p.nnz = a.nnz;
+        p.nqb = (L.N + kQ_BQ - 1) / kQ_BQ;
         p.c = c;
         p.scale = a.scale;
-        const int64_t grid = (int64_t)a.B * a.H * p.nqb;
+        const int64_t grid = (int64_t)L.B * L.H * p.nqb;
         hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
         return hipGetLastError();
     }
@@ -513,7 +599,7 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
-    if (a.d == 64) return a.causal ? launch_all<64, true>(a, stream) : launch_all<64, false>(a, stream);
+    if (a.L.d == 64) return a.causal ? launch_all<64, true>(a, stream) : launch_all<64, false>(a, stream);
     return a.causal ? launch_all<128, true>(a, stream) : launch_all<128, false>(a, stream);
 }
 

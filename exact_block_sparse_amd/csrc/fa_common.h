@@ -112,6 +112,38 @@ __device__ __forceinline__ uint32_t rows_bytes(int r0, int n, int64_t sn, int d,
     return (uint32_t)(((int64_t)last * sn + d) * 2);
 }
 
+// Where one sequence lives. Fixed length (cu == nullptr): sequence b is the b-th [N, d]
+// slab of each tensor. Packed variable length: rows cu[b] .. cu[b+1]-1 of the packed
+// tensors, clamped to [0, total) and to at most N rows, so that no access leaves the
+// tensors whatever the offsets hold.
+struct SeqSpan {
+    int64_t tok0;   // first packed row (packed mode)
+    int len;        // rows of this sequence
+    bool packed;
+};
+__device__ __forceinline__ SeqSpan seq_span(const int32_t* cu, int64_t total, int b, int N) {
+    SeqSpan s{0, N, false};
+    if (cu) {
+        int64_t lo = cu[b], hi = cu[b + 1];
+        lo = lo < 0 ? 0 : (lo > total ? total : lo);
+        hi = hi < lo ? lo : (hi > total ? total : hi);
+        const int64_t n = hi - lo;
+        s.tok0 = lo;
+        s.len = (int)(n < N ? n : N);
+        s.packed = true;
+    }
+    return s;
+}
+// Element offset of row 0 of sequence b, head h, in a tensor with strides (sb, sh, sn).
+__device__ __forceinline__ int64_t seq_off(const SeqSpan& s, int b, int h, int64_t sb, int64_t sh, int64_t sn) {
+    return (s.packed ? s.tok0 * sn : (int64_t)b * sb) + (int64_t)h * sh;
+}
+// Offset of the first per-row statistic (LSE, D) of sequence b, head h: [B, H, N] for fixed
+// length, [H, total] when packed.
+__device__ __forceinline__ int64_t seq_stat_off(const SeqSpan& s, int b, int h, int H, int N, int64_t total) {
+    return s.packed ? (int64_t)h * total + s.tok0 : ((int64_t)b * H + h) * N;
+}
+
 // ds_read_b64_tr_b16 (gfx950): each lane supplies the LDS address of 4 consecutive bf16.
 // Within every group of 16 lanes, lane i receives element (i % 4) of the chunks addressed
 // by lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4. So if lane j of a group addresses

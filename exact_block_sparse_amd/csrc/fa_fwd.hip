@@ -64,7 +64,10 @@ struct Params {
     uint16_t* o;
     float* lse;
     int64_t qsb, qsh, qsn, ksb, ksh, ksn, vsb, vsh, vsn, osb, osh, osn;
-    int B, H, N;
+    int B, H, N;      // N: rows per sequence (packed: the longest sequence's bound)
+    int G;            // query heads per K/V head
+    const int32_t* cu;   // packed sequence offsets [B + 1], or nullptr
+    int64_t total;       // packed rows
     int nqb;          // query blocks (of the workgroup's row count) per head
     float c;          // scale * log2(e)
     const int32_t* kv_offsets;
@@ -254,16 +257,16 @@ __device__ __forceinline__ void load_q(Rows<D>& w, const uint16_t* qp, int64_t q
     w.l_part = 0.0f;
 }
 
-// O = O^T / l as bf16; LSE = (m + log2 l) * ln 2.
+// O = O^T / l as bf16; LSE = (m + log2 l) * ln 2. `obase` and `lbase` point at row 0 of the
+// sequence's head.
 template <int D>
-__device__ __forceinline__ void epilogue(const Rows<D>& w, const Params& p, int b, int hh, int bh, int qrow,
-                                         int hf) {
+__device__ __forceinline__ void epilogue(const Rows<D>& w, uint16_t* obase, int64_t osn, float* lbase, int qrow,
+                                         int N, int hf) {
     using C = Cfg<D>;
     const float l_tot = pair_sum(w.l_part);
-    const int N = p.N;
     if (qrow >= N) return;
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    uint16_t* orow = p.o + b * p.osb + hh * p.osh + (int64_t)qrow * p.osn;
+    uint16_t* orow = obase + (int64_t)qrow * osn;
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
@@ -275,7 +278,7 @@ __device__ __forceinline__ void epilogue(const Rows<D>& w, const Params& p, int 
             val[3] = (__bf16)(w.o[cb][4 * j + 3] * inv);
             *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * j + 4 * hf) = val;
         }
-    if (hf == 0) p.lse[(int64_t)bh * N + qrow] = l_tot > 0.0f ? (w.m_run + log2f(l_tot)) * kLn2 : kNegInf;
+    if (hf == 0) lbase[qrow] = l_tot > 0.0f ? (w.m_run + log2f(l_tot)) * kLn2 : kNegInf;
 }
 
 // ----------------------------------------------------------------------------- dense, ping-pong
@@ -297,18 +300,21 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_kernel(Params p) {
     int qblk = logical % p.nqb;
     if (CAUSAL) qblk = p.nqb - 1 - qblk;   // longest query blocks first
     const int b = bh / p.H, hh = bh % p.H;
-    const int N = p.N;
-
-    const uint16_t* kp = p.k + b * p.ksb + hh * p.ksh;
-    const uint16_t* vp = p.v + b * p.vsb + hh * p.vsh;
-
+    const SeqSpan sp = seq_span(p.cu, p.total, b, p.N);
+    const int N = sp.len;
     const int q0 = qblk * kPPRows;
+    if (q0 >= N) return;   // past the end of a shorter packed sequence (uniform per workgroup)
+
+    const int hk = hh / p.G;
+    const uint16_t* kp = p.k + seq_off(sp, b, hk, p.ksb, p.ksh, p.ksn);
+    const uint16_t* vp = p.v + seq_off(sp, b, hk, p.vsb, p.vsh, p.vsn);
+
     const int qw0 = q0 + 32 * wave;
     const int qrow = qw0 + i;
     const int qlast = min(q0 + kPPRows - 1, N - 1);
 
     Rows<D> w;
-    load_q<D>(w, p.q + b * p.qsb + hh * p.qsh, p.qsn, qrow, N, hf);
+    load_q<D>(w, p.q + seq_off(sp, b, hh, p.qsb, p.qsh, p.qsn), p.qsn, qrow, N, hf);
 
     int T = (N + kBK - 1) / kBK;
     if (CAUSAL) T = min(T, qlast / kBK + 1);
@@ -356,7 +362,8 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_kernel(Params p) {
         }
         __syncthreads();
     }
-    epilogue<D>(w, p, b, hh, bh, qrow, hf);
+    epilogue<D>(w, p.o + seq_off(sp, b, hh, p.osb, p.osh, p.osn), p.osn,
+                p.lse + seq_stat_off(sp, b, hh, p.H, p.N, p.total), qrow, N, hf);
 }
 
 // ----------------------------------------------------------------------------- sparse
@@ -374,18 +381,21 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
     const int bh = logical / p.nqb;
     const int qblk = p.nqb - 1 - logical % p.nqb;   // longest lists first
     const int b = bh / p.H, hh = bh % p.H;
-    const int N = p.N;
-
-    const uint16_t* kp = p.k + b * p.ksb + hh * p.ksh;
-    const uint16_t* vp = p.v + b * p.vsb + hh * p.vsh;
-
+    const SeqSpan sp = seq_span(p.cu, p.total, b, p.N);
+    const int N = sp.len;
     const int q0 = qblk * kSparseBlock;
+    if (q0 >= N) return;   // past the end of a shorter packed sequence (uniform per workgroup)
+
+    const int hk = hh / p.G;
+    const uint16_t* kp = p.k + seq_off(sp, b, hk, p.ksb, p.ksh, p.ksn);
+    const uint16_t* vp = p.v + seq_off(sp, b, hk, p.vsb, p.vsh, p.vsn);
+
     const int qw0 = q0 + 32 * wave;
     const int qrow = qw0 + i;
     const int qlast = min(q0 + kSparseBlock - 1, N - 1);
 
     Rows<D> w;
-    load_q<D>(w, p.q + b * p.qsb + hh * p.qsh, p.qsn, qrow, N, hf);
+    load_q<D>(w, p.q + seq_off(sp, b, hh, p.qsb, p.qsh, p.qsn), p.qsn, qrow, N, hf);
 
     // Step t covers half (t & 1) of the listed key block kv_indices[t >> 1]. Offsets are
     // clamped to [0, nnz]; out-of-range and (causal) above-diagonal entries are skipped.
@@ -439,7 +449,8 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
         t = tn;
         kt = ktn;
     }
-    epilogue<D>(w, p, b, hh, bh, qrow, hf);
+    epilogue<D>(w, p.o + seq_off(sp, b, hh, p.osb, p.osh, p.osn), p.osn,
+                p.lse + seq_stat_off(sp, b, hh, p.H, p.N, p.total), qrow, N, hf);
 }
 
 template <int D>
@@ -475,14 +486,17 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     p.ksb = a.k.sb; p.ksh = a.k.sh; p.ksn = a.k.sn;
     p.vsb = a.v.sb; p.vsh = a.v.sh; p.vsn = a.v.sn;
     p.osb = a.osb; p.osh = a.osh; p.osn = a.osn;
-    p.B = a.B; p.H = a.H; p.N = a.N;
+    p.B = a.L.B; p.H = a.L.H; p.N = a.L.N;
+    p.G = a.L.H / a.L.Hkv;
+    p.cu = a.L.cu;
+    p.total = a.L.total;
     p.nqb = 0;
     p.c = a.scale * kLog2e;
     p.kv_offsets = a.kv_offsets;
     p.kv_indices = a.kv_indices;
     p.nnz = a.nnz;
     const bool sparse = a.kv_offsets != nullptr;
-    if (a.d == 64) return dispatch<64>(p, a.causal != 0, sparse, stream);
+    if (a.L.d == 64) return dispatch<64>(p, a.causal != 0, sparse, stream);
     return dispatch<128>(p, a.causal != 0, sparse, stream);
 }
 

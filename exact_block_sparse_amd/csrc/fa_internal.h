@@ -13,12 +13,23 @@ struct View {
     int64_t sb, sh, sn;
 };
 
+// Sequence layout shared by the forward and backward arguments. Fixed length: sequence b
+// is the b-th [N, d] slab of every tensor (batch stride). Packed variable length
+// (cu != nullptr): sequence b is rows cu[b] .. cu[b+1]-1 of [total, d] tensors (the batch
+// stride is unused), at most N rows long; LSE and D are then [H, total].
+// Grouped heads: K, V (and dK, dV) have Hkv heads; query head h reads head h / (H / Hkv).
+struct Layout {
+    int B, H, Hkv, N, d;
+    const int32_t* cu;
+    int64_t total;
+};
+
 struct FwdArgs {
+    Layout L;
     View q, k, v;
     void* o;
     int64_t osb, osh, osn;
     float* lse;
-    int B, H, N, d;
     int causal;
     float scale;
     // block-sparse mode (kv_offsets != nullptr)
@@ -36,10 +47,17 @@ struct BwdArgs {
     int64_t dksb, dksh, dksn;
     void* dv;
     int64_t dvsb, dvsh, dvsn;
-    float* delta;  // workspace: fp32 [B, H, N]
-    int B, H, N, d;
+    float* delta;  // workspace: fp32, laid out like the LSE
+    Layout L;
     int causal;
     float scale;
+    // block-sparse mode (kv_offsets != nullptr): query-side lists for dQ, key-side lists
+    // (for every key block, the query blocks that list it) for dK and dV; nnz entries each.
+    const int32_t* kv_offsets;
+    const int32_t* kv_indices;
+    const int32_t* q_offsets;
+    const int32_t* q_indices;
+    int64_t nnz;
 };
 
 // Launch the forward kernels on `stream`; returns hipSuccess or the launch error.

@@ -151,6 +151,97 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, co
            int causal, float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_attn_desc - the general problem description taken by fa_attn_fwd, fa_attn_bwd and
+ * fa_attn_bwd_workspace_bytes. It extends the calls above in three ways, each of which
+ * leaves the computed function exact attention:
+ *
+ * Grouped key/value heads ("Flash MSA Attention Kernel Implementation: A Practical Guide
+ * for Production AI", FAQ on grouped-query and multi-query attention: the tiling is the
+ * same, K and V heads are shared by several query heads). K, V, dK and dV have H_kv heads;
+ * query head h reads K/V head h / (H / H_kv) (consecutive query heads share a K/V head;
+ * H_kv = H is plain multi-head attention, H_kv = 1 multi-query attention). dK and dV of a
+ * K/V head are the sums over the query heads that read it.
+ *
+ * Packed variable-length sequences (same page, production notes on request batching: the
+ * softmax of every tile ignores padding; and its FAQ on the varlen entry point). With
+ * cu_seqlens != NULL the B sequences are packed one after another along the token axis of
+ * [total, heads, d] tensors: sequence b is rows cu_seqlens[b] .. cu_seqlens[b+1]-1 and
+ * attends only to itself (causal positions and block numbers count from its first row).
+ * Element (row r, head h, c) of a packed tensor lives at ptr + r*stride.n + h*stride.h + c;
+ * stride.b is unused. N is then an upper bound on every sequence's length (the longest
+ * sequence); rows of a longer sequence past N are not computed. LSE (and the backward
+ * workspace) are fp32 [H, total]. The kernels clamp the offsets to [0, total], so any
+ * offset values keep every access inside the tensors; the caller must still pass
+ * ascending offsets with cu_seqlens[0] = 0 and cu_seqlens[B] <= total to get results.
+ *
+ * Block-sparse masks (as in fa_sparse_fwd) with kv_offsets != NULL. For the backward
+ * ("How Does Flash-MSA Sparse Attention Work", FAQ on training: the backward reuses the
+ * forward's tiling and masking and recomputes the scores) the dK/dV pass also needs the
+ * same pattern seen from the key side: q_offsets / q_indices, for every key block the
+ * ascending query blocks whose lists name it, as produced by fa_transpose_block_lists.
+ * With packed sequences the lists apply to every sequence, block numbers counted from the
+ * sequence's first row; they must cover ceil(N / block_size) blocks.
+ */
+typedef struct fa_attn_desc {
+    int64_t B;                  /* sequences (batch)                                          */
+    int64_t H;                  /* query heads                                                */
+    int64_t H_kv;               /* key/value heads, H % H_kv == 0 (else FA_ERR_SHAPE)          */
+    int64_t N;                  /* tokens per sequence; packed: upper bound on every length    */
+    int64_t d;                  /* head dimension, 64 or 128                                   */
+    int causal;                 /* nonzero: key j allowed for query i only if j <= i           */
+    float scale;                /* score multiplier, finite                                    */
+    const int32_t* cu_seqlens;  /* NULL, or device int32 [B + 1]: packed sequence offsets     */
+    int64_t total;              /* packed mode: rows of the packed tensors                     */
+    int64_t block_size;         /* block-sparse mode: 128                                      */
+    const int32_t* kv_offsets;  /* NULL (dense), or device int32 [nb + 1]: query-side lists    */
+    const int32_t* kv_indices;  /* device int32 [nnz]                                          */
+    int64_t nnz;                /* entries of kv_indices (and of q_indices)                    */
+    const int32_t* q_offsets;   /* backward, block-sparse: device int32 [nb + 1], key side     */
+    const int32_t* q_indices;   /* device int32 [nnz]                                          */
+} fa_attn_desc;
+
+/*
+ * fa_attn_fwd - forward with log-sum-exp write-out for any fa_attn_desc (the function of
+ * fa_fwd, or of fa_sparse_fwd when kv_offsets != NULL, with grouped heads and packed
+ * sequences as described there). q, o: H heads; k, v: H_kv heads. lse: fp32 [B, H, N]
+ * contiguous, or [H, total] when packed. Errors as in fa_fwd and fa_sparse_fwd; FA_ERR_SHAPE
+ * also for H not a multiple of H_kv or a bad total; FA_ERR_NULL for NULL desc.
+ */
+FA_API int fa_attn_fwd(const fa_attn_desc* desc, const void* q, fa_strides sq, const void* k, fa_strides sk,
+                       const void* v, fa_strides sv, void* o, fa_strides so, float* lse, void* stream);
+
+/*
+ * fa_attn_bwd_workspace_bytes - device workspace fa_attn_bwd needs: one fp32 per query row
+ * and query head (H * B * N, or H * total when packed) times 4 bytes, rounded up to 256.
+ * 0 for an empty problem or a NULL desc.
+ */
+FA_API size_t fa_attn_bwd_workspace_bytes(const fa_attn_desc* desc);
+
+/*
+ * fa_attn_bwd - backward by recomputation (the function of fa_bwd) for any fa_attn_desc:
+ * grouped heads (dk, dv have H_kv heads and sum over their query heads), packed sequences,
+ * and block-sparse masks (kv_offsets / kv_indices for dQ, q_offsets / q_indices for dK and
+ * dV; both describe the same pattern, which must be the one the forward used). o and lse
+ * are the forward's outputs for the same desc. The kernels are deterministic (no atomics).
+ * Errors as in fa_bwd; FA_ERR_NULL also when block-sparse and q_offsets is NULL.
+ */
+FA_API int fa_attn_bwd(const fa_attn_desc* desc, const void* q, fa_strides sq, const void* k, fa_strides sk,
+                       const void* v, fa_strides sv, const void* o, fa_strides so, const void* dout,
+                       fa_strides sdo, const float* lse, void* dq, fa_strides sdq, void* dk, fa_strides sdk,
+                       void* dv, fa_strides sdv, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_transpose_block_lists - host: the key-side form of CSR block lists. For every key
+ * block kb, t_indices[t_offsets[kb] .. t_offsets[kb+1]) lists in ascending order the query
+ * blocks whose lists name kb (the walk the backward's dK/dV pass makes; "How Does
+ * Flash-MSA Sparse Attention Work", FAQ on training). The input must pass
+ * fa_check_block_lists (causal = 0), else FA_ERR_LIST. All pointers host; t_offsets has
+ * n_blocks + 1 entries, t_indices nnz.
+ */
+FA_API int fa_transpose_block_lists(int64_t n_blocks, const int32_t* offsets, const int32_t* indices, int64_t nnz,
+                                    int32_t* t_offsets, int32_t* t_indices);
+
+/*
  * fa_make_block_lists - host generator of the block-sparse pattern used with fa_sparse_fwd.
  *
  * "How Does Flash-MSA Sparse Attention Work", section "How Flash-MSA Sparse Attention

@@ -293,3 +293,42 @@ def attention_backward_varlen(Q, K, V, dO, cu_seqlens, *, causal: bool, scale: f
     if return_forward:
         return dQ, dK, dV, O, LSE
     return dQ, dK, dV
+
+
+def backward_keys_dkdv(Q, K, V, dO, *, causal: bool, scale: float, sparse: dict | None = None, b: int = 0,
+                       h_kv: int = 0, keys=(), rows=None):
+    """dK and dV of selected keys of K/V head ``h_kv`` (summed over the query heads that read
+    it), for checks at sizes where the whole backward is too slow.
+
+    Every query row i that may see a selected key contributes scale * dS_ij q_i to dK_j and
+    P_ij dO_i to dV_j; P_ij and D_i need i's whole row. ``rows``: the query rows to visit
+    (default all); rows that cannot see any selected key add nothing, so a superset is fine.
+    Returns {key: (dK_j, dV_j)}.
+    """
+    B, H, N, d = Q.shape
+    H_kv = K.shape[1]
+    G = H // H_kv
+    if kv_head(0, H, H_kv) != 0:   # validates the grouping
+        raise ValueError("bad head grouping")
+    Kb, Vb = _f64(K[b, h_kv]), _f64(V[b, h_kv])
+    want = sorted(set(int(j) for j in keys))
+    acc = {j: (np.zeros(K.shape[-1]), np.zeros(V.shape[-1])) for j in want}
+    ks = KeySets(N, causal, sparse)
+    row_list = range(N) if rows is None else sorted(set(int(r) for r in rows))
+    for h in range(h_kv * G, (h_kv + 1) * G):
+        Qh, dOh = _f64(Q[b, h]), _f64(dO[b, h])
+        for i in row_list:
+            J = ks.keys(i)
+            hit = np.intersect1d(J, want, assume_unique=True)
+            if hit.size == 0:
+                continue
+            s = row_scores(Qh[i], Kb, J, scale)
+            p, _, _ = row_probabilities(s)
+            dp = Vb[J] @ dOh[i]
+            Di = float(p @ dp)
+            pos = np.searchsorted(J, hit)
+            for j, t in zip(hit, pos):
+                ds = p[t] * (dp[t] - Di)
+                acc[int(j)][0][:] += scale * ds * Qh[i]
+                acc[int(j)][1][:] += p[t] * dOh[i]
+    return acc

@@ -154,3 +154,101 @@ def test_make_block_lists_capacity(fa):
     assert st == 9 and nnz.value > 3
     assert fa.lib.fa_make_block_lists(10, -1, 4, 1, 0, off.ctypes.data_as(p), idx.ctypes.data_as(p), 3,
                                       ctypes.byref(nnz)) == 8
+
+
+# ----------------------------------------------------------------------------- general entry points
+def make_desc(fa, **kw):
+    x = fa.AttnDesc()
+    x.B, x.H, x.H_kv, x.N, x.d, x.causal, x.scale = 1, 4, 2, 64, 128, 1, 0.1
+    for k, v in kw.items():
+        setattr(x, k, v)
+    return x
+
+
+def call_attn_fwd(fa, desc, q=16, k=16, v=16, o=16, lse=16, st=(8192, 8192, 128)):
+    s = strides(*st)
+    d = ctypes.byref(desc) if desc is not None else None
+    return fa.lib.fa_attn_fwd(d, ctypes.c_void_p(q), s, ctypes.c_void_p(k), s, ctypes.c_void_p(v), s,
+                              ctypes.c_void_p(o), s, ctypes.c_void_p(lse), None)
+
+
+def call_attn_bwd(fa, desc, ws=16, ws_bytes=1 << 30):
+    s = strides(8192, 8192, 128)
+    p = ctypes.c_void_p(16)
+    d = ctypes.byref(desc) if desc is not None else None
+    return fa.lib.fa_attn_bwd(d, p, s, p, s, p, s, p, s, p, s, p, p, s, p, s, p, s, ctypes.c_void_p(ws), ws_bytes,
+                              None)
+
+
+def test_attn_desc_layout_matches_header(fa):
+    # int64 x5, int + float sharing one 8-byte slot, then 8-byte pointers and int64s: 14 slots
+    assert ctypes.sizeof(fa.AttnDesc) == 8 * 14
+    assert fa.AttnDesc.cu_seqlens.offset == 48 and fa.AttnDesc.q_indices.offset == 104
+
+
+def test_attn_fwd_argument_errors(fa):
+    assert call_attn_fwd(fa, None) == 1                                  # NULL desc
+    assert call_attn_fwd(fa, make_desc(fa, H_kv=3)) == 2                 # H not a multiple of H_kv
+    assert call_attn_fwd(fa, make_desc(fa, H_kv=0)) == 2
+    assert call_attn_fwd(fa, make_desc(fa, H_kv=-1)) == 2
+    assert call_attn_fwd(fa, make_desc(fa, d=80)) == 3
+    assert call_attn_fwd(fa, make_desc(fa, scale=float("nan"))) == 8
+    assert call_attn_fwd(fa, make_desc(fa, cu_seqlens=16, total=-5)) == 2
+    assert call_attn_fwd(fa, make_desc(fa), q=8) == 4                    # misaligned
+    assert call_attn_fwd(fa, make_desc(fa), lse=0) == 1
+    assert call_attn_fwd(fa, make_desc(fa, kv_indices=16)) == 1          # lists without offsets
+    assert call_attn_fwd(fa, make_desc(fa, kv_offsets=16, block_size=64)) == 2
+    assert call_attn_fwd(fa, make_desc(fa, kv_offsets=16, block_size=128, nnz=-1)) == 5
+    assert call_attn_fwd(fa, make_desc(fa, kv_offsets=16, block_size=128, nnz=4)) == 1   # no indices
+    # empty problems: nothing launched, no device needed
+    assert call_attn_fwd(fa, make_desc(fa, B=0), q=0) == 0
+    assert call_attn_fwd(fa, make_desc(fa, cu_seqlens=16, total=0), q=0) == 0
+
+
+def test_attn_bwd_argument_errors(fa):
+    assert call_attn_bwd(fa, None) == 1
+    assert call_attn_bwd(fa, make_desc(fa, H=6, H_kv=4)) == 2
+    sparse = dict(kv_offsets=16, kv_indices=16, block_size=128, nnz=4)
+    assert call_attn_bwd(fa, make_desc(fa, **sparse)) == 1               # key-side lists missing
+    assert "q_offsets" in fa.lib.fa_last_error().decode()
+    assert call_attn_bwd(fa, make_desc(fa, q_offsets=16, **sparse)) == 1
+    assert call_attn_bwd(fa, make_desc(fa), ws=0) == 6
+    assert call_attn_bwd(fa, make_desc(fa), ws_bytes=100) == 6
+
+
+def test_attn_workspace_bytes(fa):
+    lib = fa.lib
+    x = make_desc(fa, B=2, H=8, H_kv=2, N=1000)
+    assert lib.fa_attn_bwd_workspace_bytes(ctypes.byref(x)) == (2 * 8 * 1000 * 4 + 255) // 256 * 256
+    x = make_desc(fa, B=3, H=8, H_kv=1, N=700, cu_seqlens=16, total=1234)
+    assert lib.fa_attn_bwd_workspace_bytes(ctypes.byref(x)) == (8 * 1234 * 4 + 255) // 256 * 256
+    assert lib.fa_attn_bwd_workspace_bytes(None) == 0
+    assert fa.attn_bwd_workspace_bytes(3, 8, 700, 128, total=1234) == (8 * 1234 * 4 + 255) // 256 * 256
+    assert fa.attn_bwd_workspace_bytes(2, 8, 1000, 128) == fa.bwd_workspace_bytes(2, 8, 1000, 128)
+
+
+@pytest.mark.parametrize("nb,window,stride,causal,rule", [(1, 0, 0, True, "strided"), (37, 2, 5, True, "strided"),
+                                                          (37, 2, 5, False, "fixed"), (64, 8, 16, True, "fixed"),
+                                                          (20, 0, 0, False, "strided")])
+def test_transposed_lists_equal_oracle(fa, nb, window, stride, causal, rule):
+    off, idx = oracle.block_lists(nb, window, stride, causal, rule)
+    t_off, t_idx = fa.transpose_block_lists(off, idx, nb)
+    o_off, o_idx = oracle.transpose_lists(off, idx, nb)
+    assert np.array_equal(t_off, o_off) and np.array_equal(t_idx, o_idx)
+
+
+def test_transposed_lists_128k(fa):
+    off, idx = fa.make_block_lists(1024, 8, 16, True, "strided")
+    t_off, t_idx = fa.transpose_block_lists(off, idx, 1024)
+    o_off, o_idx = oracle.transpose_lists(off, idx, 1024)
+    assert np.array_equal(t_off, o_off) and np.array_equal(t_idx, o_idx) and t_off[-1] == 41436
+
+
+def test_transpose_rejects_malformed(fa):
+    with pytest.raises(fa.FaError) as e:
+        fa.transpose_block_lists(np.array([0, 2, 3], np.int32), np.array([1, 0, 0], np.int32), 2)   # unsorted
+    assert e.value.status == 5
+    with pytest.raises(fa.FaError):
+        fa.transpose_block_lists(np.array([0, 1, 2], np.int32), np.array([0, 2], np.int32), 2)      # out of range
+    empty = fa.transpose_block_lists(np.zeros(4, np.int32), np.zeros(0, np.int32), 3)
+    assert np.array_equal(empty[0], np.zeros(4, np.int32)) and empty[1].size == 0

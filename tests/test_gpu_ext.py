@@ -1,0 +1,416 @@
+"""GPU parity of the general entry points (fa_attn_fwd / fa_attn_bwd) against the fp64 oracle:
+grouped K/V heads (GQA, MQA), packed variable-length sequences, and the block-sparse
+backward with key-side lists; each alone and combined.
+
+Small cases are compared element by element; the extension workloads are compared at
+full size on sampled query rows (O, LSE, dQ) and sampled keys (dK, dV, summed over the
+query heads of a group). Tolerances as everywhere: max-abs 2e-2 on O, dQ, dK, dV, 1e-3
+on LSE.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import TOL_LSE, TOL_OUT, assert_close, assert_finite, f64, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write(f"\n[gpu-case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+
+
+@pytest.fixture(scope="module")
+def fa():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import exact_block_sparse_amd as fa
+    return fa
+
+
+def dev(x):
+    return {n: t.to("cuda") for n, t in x.items()}
+
+
+def lists_for(n_blocks, window, stride, causal, rule="strided"):
+    off, idx = oracle.block_lists(n_blocks, window, stride, causal, rule)
+    return off, idx, dict(block=128, offsets=off, indices=idx)
+
+
+# ----------------------------------------------------------------------------- grouped heads
+GQA_FWD = [
+    # B, H, H_kv, N, d, causal, layout
+    (2, 8, 2, 300, 128, True, "bhnd"),
+    (1, 6, 3, 200, 64, False, "bnhd"),
+    (1, 4, 1, 129, 128, True, "bhnd"),      # multi-query
+    (1, 4, 4, 100, 128, True, "bhnd"),      # H_kv = H through the general call
+    (1, 8, 2, 513, 64, True, "bhnd"),
+]
+
+
+@pytest.mark.parametrize("case", GQA_FWD, ids=lambda c: "b{}h{}kv{}n{}d{}{}{}".format(
+    c[0], c[1], c[2], c[3], c[4], "c" if c[5] else "", c[6]))
+def test_gqa_forward_small(fa, case):
+    B, H, Hkv, N, d, causal, layout = case
+    w = W.small(B, H, N, d, causal=causal, layout=layout, seed=11, H_kv=Hkv)
+    x = W.make_inputs(w)
+    g = dev(x)
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_forward(x["q"], x["k"], x["v"], causal=causal, scale=w.scale)
+    assert_close("O", o, O, TOL_OUT)
+    assert_close("LSE", lse, L, TOL_LSE)
+
+
+def test_gqa_with_shared_heads_equals_replicated_mha(fa):
+    # grouping only changes which K/V head is read: the same numbers as plain multi-head
+    # attention on K/V replicated over the group (same kernels, same order of work)
+    w = W.small(1, 8, 700, 128, causal=True, seed=12, H_kv=2)
+    g = dev(W.make_inputs(w))
+    o1, l1 = fa.attn_fwd(g["q"], g["k"], g["v"], causal=True, scale=w.scale)
+    kr = g["k"].repeat_interleave(4, dim=1).contiguous()
+    vr = g["v"].repeat_interleave(4, dim=1).contiguous()
+    o2, l2 = fa.fwd(g["q"], kr, vr, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# dK and dV of a K/V head sum over its query heads, so they grow with the group; the
+# multi-query case is drawn at sigma 0.5 to keep |dV| below 8, where bf16 output rounding
+# (half an ulp is 1/32 from 8 up) would exceed the 2e-2 bound on its own.
+GQA_BWD = [
+    (1, 4, 2, 200, 128, True, 1.0),
+    (2, 6, 3, 130, 64, False, 1.0),
+    (1, 4, 1, 257, 128, True, 0.5),
+]
+
+
+@pytest.mark.parametrize("case", GQA_BWD, ids=lambda c: "b{}h{}kv{}n{}d{}{}".format(
+    c[0], c[1], c[2], c[3], c[4], "c" if c[5] else ""))
+def test_gqa_backward_small(fa, case):
+    B, H, Hkv, N, d, causal, sigma = case
+    w = W.small(B, H, N, d, causal=causal, seed=13, H_kv=Hkv, direction="bwd", sigma=sigma)
+    x = W.make_inputs(w)
+    g = dev(x)
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], causal=causal, scale=w.scale)
+    dq, dk, dv = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert tuple(dk.shape) == tuple(x["k"].shape)
+    dQ, dK, dV = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], causal=causal, scale=w.scale)
+    assert_close("dQ", dq, dQ, TOL_OUT)
+    assert_close("dK", dk, dK, TOL_OUT)
+    assert_close("dV", dv, dV, TOL_OUT)
+
+
+# ----------------------------------------------------------------------------- packed sequences
+VARLEN = [
+    # lengths, H, H_kv, d, causal
+    ((37, 0, 263, 1, 399), 4, 2, 128, True),
+    ((37, 0, 263, 1, 399), 2, 2, 128, False),
+    ((128, 128, 128), 2, 1, 64, True),
+    ((700,), 2, 2, 64, False),
+    ((5, 300, 64, 129), 3, 3, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=lambda c: "{}_h{}kv{}d{}{}".format(
+    "-".join(map(str, c[0])), c[1], c[2], c[3], "c" if c[4] else ""))
+def test_varlen_forward_small(fa, case):
+    lens, H, Hkv, d, causal = case
+    w = W.small(H=H, d=d, causal=causal, seed=14, H_kv=Hkv, seqlens=lens)
+    x = W.make_inputs(w)
+    g = dev(x)
+    cu = w.cu_seqlens()
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], causal=causal, scale=w.scale, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    assert tuple(lse.shape) == (H, w.total)
+    O, L = oracle.attention_forward_varlen(x["q"], x["k"], x["v"], cu, causal=causal, scale=w.scale)
+    assert_close("O", o, O, TOL_OUT)
+    assert_close("LSE", lse, L, TOL_LSE)
+
+
+def test_varlen_single_sequence_equals_fixed_length(fa):
+    # one packed sequence is the fixed-length problem with B = 1 in (B, N, H, d) memory
+    w = W.small(H=4, d=128, causal=True, seed=15, seqlens=(1000,))
+    g = dev(W.make_inputs(w))
+    o1, l1 = fa.attn_fwd(g["q"], g["k"], g["v"], causal=True, scale=w.scale, cu_seqlens=w.cu_seqlens())
+    view = lambda t: t.unsqueeze(0).permute(0, 2, 1, 3)
+    o2, l2 = fa.fwd(view(g["q"]), view(g["k"]), view(g["v"]), causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2[0].permute(1, 0, 2)) and torch.equal(l1, l2[0])
+
+
+@pytest.mark.parametrize("case", [((37, 0, 200, 1), 4, 2, 128, True), ((64, 100), 2, 2, 64, False),
+                                  ((129, 3, 256), 2, 1, 128, True)],
+                         ids=lambda c: "{}_h{}kv{}d{}{}".format("-".join(map(str, c[0])), c[1], c[2], c[3],
+                                                                "c" if c[4] else ""))
+def test_varlen_backward_small(fa, case):
+    # sigma 0.5: a one-row sequence makes dV the plain sum of its query heads' dO, which at
+    # sigma 1 reaches the 4..8 range where bf16 output rounding alone uses 0.016 of the 0.02
+    lens, H, Hkv, d, causal = case
+    w = W.small(H=H, d=d, causal=causal, seed=16, H_kv=Hkv, seqlens=lens, direction="bwd", sigma=0.5)
+    x = W.make_inputs(w)
+    g = dev(x)
+    cu = w.cu_seqlens()
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], causal=causal, scale=w.scale, cu_seqlens=cu)
+    dq, dk, dv = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], causal=causal, scale=w.scale,
+                             cu_seqlens=cu)
+    torch.cuda.synchronize()
+    dQ, dK, dV = oracle.attention_backward_varlen(x["q"], x["k"], x["v"], x["do"], cu, causal=causal,
+                                                  scale=w.scale)
+    assert_close("dQ", dq, dQ, TOL_OUT)
+    assert_close("dK", dk, dK, TOL_OUT)
+    assert_close("dV", dv, dV, TOL_OUT)
+
+
+def test_varlen_device_offsets_and_trailing_rows(fa):
+    # offsets as a device tensor with max_seqlen given; packed rows after the last sequence
+    # are not part of any sequence and are left as they were
+    w = W.small(H=2, d=64, causal=True, seed=17, seqlens=(100, 50, 30))
+    x = W.make_inputs(w)
+    pad = 20
+    q, k, v = (torch.cat([x[n], torch.zeros(pad, *x[n].shape[1:], dtype=x[n].dtype)]).to("cuda") for n in "qkv")
+    cu = torch.tensor(w.cu_seqlens(), dtype=torch.int32, device="cuda")
+    out = torch.full_like(q, 7.0)
+    o, lse = fa.attn_fwd(q, k, v, causal=True, scale=w.scale, cu_seqlens=cu, max_seqlen=100, out=out)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_forward_varlen(x["q"], x["k"], x["v"], w.cu_seqlens(), causal=True, scale=w.scale)
+    assert_close("O", o[: w.total], O, TOL_OUT)
+    assert_close("LSE", lse[:, : w.total], L, TOL_LSE)
+    assert bool((o[w.total:] == 7.0).all())
+
+
+# ----------------------------------------------------------------------------- block-sparse backward
+SPARSE_BWD = [
+    # N, H, H_kv, d, causal, window, stride, rule
+    (1000, 2, 2, 128, True, 1, 3, "strided"),
+    (640, 2, 2, 64, False, 1, 2, "fixed"),
+    (900, 4, 2, 128, True, 2, 4, "strided"),
+    (256, 1, 1, 128, True, 0, 0, "strided"),
+]
+
+
+@pytest.mark.parametrize("case", SPARSE_BWD, ids=lambda c: "n{}h{}kv{}d{}{}w{}s{}{}".format(
+    c[0], c[1], c[2], c[3], "c" if c[4] else "", c[5], c[6], c[7]))
+def test_sparse_backward_small(fa, case):
+    N, H, Hkv, d, causal, window, stride, rule = case
+    w = W.small(1, H, N, d, causal=causal, seed=18, H_kv=Hkv, direction="bwd")
+    x = W.make_inputs(w)
+    g = dev(x)
+    nb = (N + 127) // 128
+    off, idx, sp = lists_for(nb, window, stride, causal, rule)
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], causal=causal, scale=w.scale, kv_offsets=off, kv_indices=idx)
+    dq, dk, dv = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], causal=causal, scale=w.scale,
+                             kv_offsets=off, kv_indices=idx)
+    torch.cuda.synchronize()
+    dQ, dK, dV, O, L = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], causal=causal, scale=w.scale,
+                                                 sparse=sp, return_forward=True)
+    assert_close("O", o, O, TOL_OUT)
+    assert_close("LSE", lse, L, TOL_LSE)
+    assert_close("dQ", dq, dQ, TOL_OUT)
+    assert_close("dK", dk, dK, TOL_OUT)
+    assert_close("dV", dv, dV, TOL_OUT)
+
+
+def test_sparse_backward_with_full_lists_equals_dense(fa):
+    # listing every causal block visits the same tiles in the same order as the dense kernels
+    w = W.small(2, 3, 777, 128, causal=True, seed=19, direction="bwd")
+    g = dev(W.make_inputs(w))
+    nb = (777 + 127) // 128
+    off, idx = fa.make_block_lists(nb, nb, 0, causal=True)
+    o, lse = fa.fwd(g["q"], g["k"], g["v"], causal=True, scale=w.scale)
+    d1 = fa.bwd(g["q"], g["k"], g["v"], o, lse, g["do"], causal=True, scale=w.scale)
+    d2 = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], causal=True, scale=w.scale, kv_offsets=off,
+                     kv_indices=idx)
+    torch.cuda.synchronize()
+    for a, b in zip(d1, d2):
+        assert torch.equal(a, b)
+
+
+def test_sparse_backward_hand_lists_with_empty_block(fa):
+    # query block 1 lists nothing: its rows have no keys (O = 0, LSE = -inf, dQ = 0) and add
+    # nothing to dK, dV; block 2 lists only block 0 (off-diagonal, fully allowed)
+    N, d = 384, 128
+    w = W.small(1, 2, N, d, causal=True, seed=20, direction="bwd")
+    x = W.make_inputs(w)
+    g = dev(x)
+    off = np.array([0, 1, 1, 2], np.int32)
+    idx = np.array([0, 0], np.int32)
+    sp = dict(block=128, offsets=off, indices=idx)
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], causal=True, scale=w.scale, kv_offsets=off, kv_indices=idx)
+    dq, dk, dv = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], causal=True, scale=w.scale,
+                             kv_offsets=off, kv_indices=idx)
+    torch.cuda.synchronize()
+    assert bool(torch.isneginf(lse[:, :, 128:256]).all())
+    assert bool((dq[:, :, 128:256] == 0).all())
+    assert_finite("dq", dq)
+    dQ, dK, dV = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], causal=True, scale=w.scale, sparse=sp)
+    assert_close("dQ", dq, dQ, TOL_OUT)
+    assert_close("dK", dk, dK, TOL_OUT)
+    assert_close("dV", dv, dV, TOL_OUT)
+
+
+def test_sparse_varlen_gqa_together(fa):
+    lens = (300, 700, 129)
+    w = W.small(H=4, d=128, causal=True, seed=21, H_kv=2, seqlens=lens, direction="bwd", sigma=0.5)
+    x = W.make_inputs(w)
+    g = dev(x)
+    cu = w.cu_seqlens()
+    nb = (max(lens) + 127) // 128
+    off, idx, sp = lists_for(nb, 1, 3, True)
+    kw = dict(causal=True, scale=w.scale, cu_seqlens=cu, kv_offsets=off, kv_indices=idx)
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], **kw)
+    dq, dk, dv = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], **kw)
+    torch.cuda.synchronize()
+    dQ, dK, dV, O, L = oracle.attention_backward_varlen(x["q"], x["k"], x["v"], x["do"], cu, causal=True,
+                                                        scale=w.scale, sparse=sp, return_forward=True)
+    assert_close("O", o, O, TOL_OUT)
+    assert_close("LSE", lse, L, TOL_LSE)
+    assert_close("dQ", dq, dQ, TOL_OUT)
+    assert_close("dK", dk, dK, TOL_OUT)
+    assert_close("dV", dv, dV, TOL_OUT)
+
+
+def test_sparse_backward_is_deterministic(fa):
+    w = W.small(1, 2, 1024, 128, causal=True, seed=22, direction="bwd")
+    g = dev(W.make_inputs(w))
+    off, idx = fa.make_block_lists(8, 1, 3, causal=True)
+    kw = dict(causal=True, scale=w.scale, kv_offsets=off, kv_indices=idx)
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], **kw)
+    a = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], **kw)
+    b = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], **kw)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+def test_workload_gqa_h32kv8_n32k(fa):
+    w = W.WORKLOADS["gqa_h32kv8_n32k"]
+    x = W.make_inputs(w)
+    g = dev(x)
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    assert_finite("o", o)
+    rows = sample_rows(w.N, 256, np.random.default_rng(6), extra=16)[::4]
+    for h in (0, 3, 4, 31):   # heads 0-3 share K/V head 0, head 4 starts K/V head 1
+        O, L = oracle.attention_forward(x["q"][:, h:h + 1], x["k"][:, h // 4:h // 4 + 1],
+                                        x["v"][:, h // 4:h // 4 + 1], causal=True, scale=w.scale, rows=rows)
+        assert_close(f"O[h{h}]", o[0, h, rows], O[0, 0, rows], TOL_OUT)
+        assert_close(f"LSE[h{h}]", lse[0, h, rows], L[0, 0, rows], TOL_LSE)
+
+
+def test_workload_gqa_bwd_b2h32kv8_n8k(fa):
+    w = W.WORKLOADS["gqa_bwd_b2h32kv8_n8k"]
+    x = W.make_inputs(w)
+    g = dev(x)
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], causal=True, scale=w.scale)
+    dq, dk, dv = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        assert_finite(n, t)
+    b, hk = 1, 5
+    rows = sample_rows(w.N, 1024, np.random.default_rng(8), extra=8)
+    ref = oracle.backward_rows_dq(x["q"], x["k"], x["v"], x["do"], causal=True, scale=w.scale, b=b, h=4 * hk + 2,
+                                  rows=rows)
+    assert_close("dQ rows", dq[b, 4 * hk + 2, rows], np.stack([ref[int(r)] for r in rows]), TOL_OUT)
+    keys = [w.N - 1, w.N - 60, w.N - 129, w.N - 200]
+    acc = oracle.backward_keys_dkdv(x["q"], x["k"], x["v"], x["do"], causal=True, scale=w.scale, b=b, h_kv=hk,
+                                    keys=keys, rows=range(min(keys), w.N))
+    assert_close("dK keys", dk[b, hk, keys], np.stack([acc[j][0] for j in keys]), TOL_OUT)
+    assert_close("dV keys", dv[b, hk, keys], np.stack([acc[j][1] for j in keys]), TOL_OUT)
+
+
+def _seq(x, cu, s, heads):
+    """(1, h, n, d) fp64 slices of packed tensors for sequence s and the given heads."""
+    a, e = int(cu[s]), int(cu[s + 1])
+    return {n: f64(t[a:e, heads]).transpose(1, 0, 2)[None] for n, t in x.items()}
+
+
+def test_workload_varlen_h32_b16(fa):
+    w = W.WORKLOADS["varlen_h32_b16"]
+    x = W.make_inputs(w)
+    g = dev(x)
+    cu = w.cu_seqlens()
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], causal=True, scale=w.scale, cu_seqlens=cu, max_seqlen=w.N)
+    torch.cuda.synchronize()
+    assert_finite("o", o)
+    rng = np.random.default_rng(7)
+    for s in (0, 8, 13, 15):
+        n = int(cu[s + 1] - cu[s])
+        rows = sample_rows(n, 256, rng, extra=8)[::3]
+        h = int(rng.integers(0, w.H))
+        sx = _seq(x, cu, s, [h])
+        O, L = oracle.attention_forward(sx["q"], sx["k"], sx["v"], causal=True, scale=w.scale, rows=rows)
+        pr = cu[s] + rows
+        assert_close(f"O[s{s}h{h}]", o[pr, h], O[0, 0, rows], TOL_OUT)
+        assert_close(f"LSE[s{s}h{h}]", lse[h, pr], L[0, 0, rows], TOL_LSE)
+
+
+def test_workload_varlen_bwd_h32_b16(fa):
+    w = W.WORKLOADS["varlen_bwd_h32_b16"]
+    x = W.make_inputs(w)
+    g = dev(x)
+    cu = w.cu_seqlens()
+    kw = dict(causal=True, scale=w.scale, cu_seqlens=cu, max_seqlen=w.N)
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], **kw)
+    dq, dk, dv = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], **kw)
+    torch.cuda.synchronize()
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        assert_finite(n, t)
+    # the shortest sequence whole (all its outputs), for two heads
+    s = int(np.argmin(np.diff(cu)))
+    heads = [0, 17]
+    sx = _seq(x, cu, s, heads)
+    dQ, dK, dV = oracle.attention_backward(sx["q"], sx["k"], sx["v"], sx["do"], causal=True, scale=w.scale)
+    a, e = int(cu[s]), int(cu[s + 1])
+    for j, h in enumerate(heads):
+        assert_close(f"dQ[s{s}h{h}]", dq[a:e, h], dQ[0, j], TOL_OUT)
+        assert_close(f"dK[s{s}h{h}]", dk[a:e, h], dK[0, j], TOL_OUT)
+        assert_close(f"dV[s{s}h{h}]", dv[a:e, h], dV[0, j], TOL_OUT)
+    # sampled dQ rows of a long sequence
+    s = int(np.argmax(np.diff(cu)))
+    sx = _seq(x, cu, s, [9])
+    n = int(cu[s + 1] - cu[s])
+    rows = sample_rows(n, 1024, np.random.default_rng(9), extra=8)
+    ref = oracle.backward_rows_dq(sx["q"], sx["k"], sx["v"], sx["do"], causal=True, scale=w.scale, rows=rows)
+    assert_close("dQ rows", dq[int(cu[s]) + rows, 9], np.stack([ref[int(r)] for r in rows]), TOL_OUT)
+
+
+def test_workload_sparse_bwd_h16_n128k(fa):
+    w = W.WORKLOADS["sparse_bwd_h16_n128k"]
+    x = W.make_inputs(w)
+    g = dev(x)
+    nb = w.N // 128
+    off, idx = fa.make_block_lists(nb, 8, 16, causal=True)
+    t_off, t_idx = fa.transpose_block_lists(off, idx, nb)
+    to = lambda a: torch.from_numpy(a).to("cuda")
+    kw = dict(causal=True, scale=w.scale, kv_offsets=to(off), kv_indices=to(idx))
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], **kw)
+    dq, dk, dv = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], q_offsets=to(t_off), q_indices=to(t_idx), **kw)
+    torch.cuda.synchronize()
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        assert_finite(n, t)
+    sp = dict(block=128, offsets=off, indices=idx)
+    h = 11
+    rows = sample_rows(w.N, 8192, np.random.default_rng(4), extra=8)
+    ref = oracle.backward_rows_dq(x["q"], x["k"], x["v"], x["do"], causal=True, scale=w.scale, sparse=sp, h=h,
+                                  rows=rows)
+    assert_close("dQ rows", dq[0, h, rows], np.stack([ref[int(r)] for r in rows]), TOL_OUT)
+    # keys of the last block (seen by one query block) and of a block 20 from the end (seen
+    # through the window and the stride): only the query blocks the key-side lists name
+    for kb in (nb - 1, nb - 20):
+        keys = [kb * 128, kb * 128 + 77, kb * 128 + 127]
+        qbs = oracle.transpose_lists(off, idx, nb)
+        qblocks = qbs[1][qbs[0][kb]:qbs[0][kb + 1]]
+        rows_k = np.concatenate([np.arange(q * 128, q * 128 + 128) for q in qblocks])
+        acc = oracle.backward_keys_dkdv(x["q"], x["k"], x["v"], x["do"], causal=True, scale=w.scale, sparse=sp,
+                                        h_kv=h, keys=keys, rows=rows_k)
+        assert_close(f"dK[kb{kb}]", dk[0, h, keys], np.stack([acc[j][0] for j in keys]), TOL_OUT)
+        assert_close(f"dV[kb{kb}]", dv[0, h, keys], np.stack([acc[j][1] for j in keys]), TOL_OUT)

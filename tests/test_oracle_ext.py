@@ -229,3 +229,26 @@ def test_transposed_lists_closed_form_at_128k():
     np.testing.assert_array_equal(lens, np.minimum(8, M) + 1 + M // 16)
     assert int(lens.sum()) == 41436
     assert all(t_idx[t_off[k]] == k for k in range(nb))   # the diagonal block always comes first
+
+
+# ----------------------------------------------------------------------------- sampled key gradients
+@pytest.mark.parametrize("sparse", [None, dict(block=8, window=1, stride=3, rule="strided")])
+def test_sampled_key_gradients_match_autograd(sparse):
+    from oracle import backward_keys_dkdv, block_lists as bl
+    g = torch.Generator().manual_seed(47)
+    H, H_kv, n, d = 4, 2, 41, 8
+    Q, dO = t64((1, H, n, d), g), t64((1, H, n, d), g)
+    K, V = t64((1, H_kv, n, d), g), t64((1, H_kv, n, d), g)
+    q, k, v = (t.clone().requires_grad_(True) for t in (Q, K, V))
+    mask = torch.tril(torch.ones(n, n, dtype=torch.bool))
+    if sparse:
+        off, idx = bl((n + 7) // 8, 1, 3, True, "strided")
+        mask &= torch.from_numpy(key_mask_from_lists(n, 8, off, idx, True))
+    S = (0.3 * q @ k.repeat_interleave(2, dim=1).transpose(-1, -2)).masked_fill(~mask, -math.inf)
+    (torch.softmax(S, -1) @ v.repeat_interleave(2, dim=1)).backward(dO)
+    keys = [0, 5, 17, 40]
+    got = backward_keys_dkdv(Q.numpy(), K.numpy(), V.numpy(), dO.numpy(), causal=True, scale=0.3, sparse=sparse,
+                             h_kv=1, keys=keys)
+    for j in keys:
+        np.testing.assert_allclose(got[j][0], k.grad[0, 1, j].numpy(), atol=1e-12)
+        np.testing.assert_allclose(got[j][1], v.grad[0, 1, j].numpy(), atol=1e-12)
