@@ -10,7 +10,7 @@ FLOP conventions: forward 4*B*H*N^2*d, halved for causal; backward 2.5x the forw
 (five matrix products against two); block-sparse: listed 128x128 tiles x 4*128*128*d
 ("counting only unmasked tiles"), with the element-exact count alongside.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads all|headline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads all|headline|KEY,...]
                        [--no-cpu-baseline]
 Prints one JSON line.
 """
@@ -243,7 +243,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="all", choices=["all", "headline"])
+    ap.add_argument("--workloads", default="all",
+                    help="all, headline, or a comma-separated list of workload keys (besides the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (to scale "
@@ -281,10 +282,14 @@ def main():
     achieved = head["flops"] / (t["mean_ms"] * 1e-3) / 1e12
 
     others = {}
-    if args.workloads == "all":
+    if args.workloads != "headline":
+        keys = W.ORDER if args.workloads == "all" else [HEADLINE] + args.workloads.split(",")
+        unknown = [k for k in keys if k not in W.WORKLOADS]
+        if unknown:
+            raise SystemExit(f"unknown workloads {unknown}; known: {W.ORDER}")
         del head["dev"]
         torch.cuda.empty_cache()
-        for key in W.ORDER:
+        for key in keys:
             if key == HEADLINE:
                 others[key] = hs
                 continue

@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
     const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, i = lane & 31;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int bhk = logical / p.nkb, kblk = logical % p.nkb;   // ascending: longest first under causal
-    const int b = bhk / p.Hkv, hk = bhk % p.Hkv;
+    const int hk = bhk / p.B, b = bhk % p.B;   // head-major: an XCD's share spans every sequence
     const SeqSpan sp = seq_span(p.cu, p.total, b, p.N);
     const int N = sp.len;
     const int k0 = kblk * kKV_BK;
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(QParams p) {
     const int bh = logical / p.nqb;
     int qb = logical % p.nqb;
     if (CAUSAL) qb = p.nqb - 1 - qb;
-    const int b = bh / p.H, hh = bh % p.H;
+    const int hh = bh / p.B, b = bh % p.B;   // head-major: an XCD's share spans every sequence
     const SeqSpan sp = seq_span(p.cu, p.total, b, p.N);
     const int N = sp.len;
     const int q0 = qb * kQ_BQ;

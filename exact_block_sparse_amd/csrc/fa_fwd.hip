@@ -299,7 +299,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_kernel(Params p) {
     const int bh = logical / p.nqb;
     int qblk = logical % p.nqb;
     if (CAUSAL) qblk = p.nqb - 1 - qblk;   // longest query blocks first
-    const int b = bh / p.H, hh = bh % p.H;
+    const int hh = bh / p.B, b = bh % p.B;   // head-major: an XCD's share spans every sequence
     const SeqSpan sp = seq_span(p.cu, p.total, b, p.N);
     const int N = sp.len;
     const int q0 = qblk * kPPRows;
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = logical / p.nqb;
     const int qblk = p.nqb - 1 - logical % p.nqb;   // longest lists first
-    const int b = bh / p.H, hh = bh % p.H;
+    const int hh = bh / p.B, b = bh % p.B;   // head-major: an XCD's share spans every sequence
     const SeqSpan sp = seq_span(p.cu, p.total, b, p.N);
     const int N = sp.len;
     const int q0 = qblk * kSparseBlock;
