@@ -195,15 +195,32 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
     const int per = sparse ? (int)(2 * (hi - lo)) : nsteps - t0;   // steps per query head
     const int n_all = per * p.G;
     const int nqb = (N + kKV_BK - 1) / kKV_BK;
-    // First query row of step s (-1: skip) and its query head.
+    // Under causal masking only the steps of the diagonal block (queries k0 .. k0+127) hold
+    // keys after queries: the first two steps of each query head (dense), or the two halves of
+    // the list's first entry when it is the diagonal block (block-sparse; lists ascend). They
+    // are taken first, for every query head, so that the rest run without the element test.
+    const int m_per = !CAUSAL ? 0 : (sparse ? ((hi > lo && p.q_indices[lo] == kblk) ? 2 : 0) : min(2, per));
+    const int n_mask = m_per * p.G;
+    const int u_per = per - m_per;
+    // First query row of step s and its query head. Entries of the key-side list that are out
+    // of range (or, causal, above the diagonal) become an empty tile at row N: its loads are
+    // zero-filled and its rows get LSE = +inf, so its probabilities are exactly 0.
     auto step_row = [&](int s, int& hq) -> int {
-        const int g = s / per, j = s - g * per;
+        int g, j;
+        if (s < n_mask) {
+            g = s / m_per;
+            j = s - g * m_per;
+        } else {
+            const int u = s - n_mask;
+            g = u / u_per;
+            j = m_per + (u - g * u_per);
+        }
         hq = hk * p.G + g;
         if (!sparse) return (t0 + j) * kStep;
         const int qb = p.q_indices[lo + (j >> 1)];
-        if (qb < 0 || qb >= nqb || (CAUSAL && qb < kblk)) return -1;
+        if (qb < 0 || qb >= nqb || (CAUSAL && qb < kblk)) return N;
         const int r0 = qb * kKV_BK + (j & 1) * kStep;
-        return r0 < N ? r0 : -1;
+        return r0 < N ? r0 : N;
     };
     const float c = p.c;
 
@@ -214,7 +231,6 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
     auto load_step = [&](int s) {
         int hq;
         const int r0 = step_row(s, hq);
-        if (r0 < 0) return;
         tq.load(p.q + seq_off(sp, b, hq, p.qsb, p.qsh, p.qsn), p.qsn, r0, N);
         td.load(p.dout + seq_off(sp, b, hq, p.dsb, p.dsh, p.dsn), p.dsn, r0, N);
         const int64_t so = seq_stat_off(sp, b, hq, p.H, p.N, p.total);
@@ -236,81 +252,132 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
         if (tid < 2 * kStep) reinterpret_cast<float*>(s + L::STATS)[tid] = st_stat;
     };
 
+    // S = Q K^T and dP = dO V^T for the 32-query subtile qb of a stage (this wave's 32 keys).
+    auto sdp = [&](const uint16_t* s, int qb, f32x16& sacc, f32x16& pacc) {
+        sacc = f32x16{};
+        pacc = f32x16{};
+        const uint16_t* qr = s + L::QR + (32 * qb + i) * C::RS + 8 * hf;
+        const uint16_t* dr = s + L::DR + (32 * qb + i) * C::RS + 8 * hf;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            sacc = mfma32(*reinterpret_cast<const bf16x8*>(qr + 16 * ks), kf[ks], sacc);
+            pacc = mfma32(*reinterpret_cast<const bf16x8*>(dr + 16 * ks), vf[ks], pacc);
+        }
+    };
+    // P = exp(S - LSE) and dS = P (dP - D) as bf16 operands. Element r of this lane is query
+    // qt0 + 32*qb + 8*(r/4) + 4*hf + r%4; with `mask`, keys after their query get P = 0.
+    auto probs = [&](bool mask, const uint16_t* s, int qb, int qt0, const f32x16& sacc, const f32x16& pacc,
+                     bf16x8 (&pb)[2], bf16x8 (&db)[2]) {
+        const float* sL = reinterpret_cast<const float*>(s + L::STATS);
+        const float* sDel = sL + kStep;
+        float pv[16], dsv[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + 32 * qb + 8 * g + 4 * hf);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(sDel + 32 * qb + 8 * g + 4 * hf);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                float pe = fast_exp2(fmaf(sacc[r], c, -l4[e]));
+                if (mask && key > qt0 + 32 * qb + acc_row(r, hf)) pe = 0.0f;
+                pv[r] = pe;
+                dsv[r] = pe * (pacc[r] - d4[e]);
+            }
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            pb[st] = pack8(pv[8 * st], pv[8 * st + 1], pv[8 * st + 2], pv[8 * st + 3], pv[8 * st + 4],
+                           pv[8 * st + 5], pv[8 * st + 6], pv[8 * st + 7]);
+            db[st] = pack8(dsv[8 * st], dsv[8 * st + 1], dsv[8 * st + 2], dsv[8 * st + 3], dsv[8 * st + 4],
+                           dsv[8 * st + 5], dsv[8 * st + 6], dsv[8 * st + 7]);
+        }
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS over the subtile's 32 queries.
+    auto grads = [&](const uint16_t* s, int qb, const bf16x8 (&pb)[2], const bf16x8 (&db)[2]) {
+        const uint16_t* qt_base = tr_lane_base(s + L::QT, C::TS, lane);
+        const uint16_t* dt_base = tr_lane_base(s + L::DT, C::TS, lane);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const int off = (32 * qb + 16 * st) * C::TS + 32 * cb;
+                dv[cb] = mfma32(read_tr_operand(dt_base, off, C::TS), pb[st], dv[cb]);
+                dk[cb] = mfma32(read_tr_operand(qt_base, off, C::TS), db[st], dk[cb]);
+            }
+    };
+
+    // Software pipeline over 32-query subtiles, so that the vector work of one subtile is
+    // issued next to independent matrix products: per step, the products S, dP of subtile 1
+    // run beside the probabilities of subtile 0, the gradient products of subtile 0 beside
+    // the probabilities of subtile 1; S, dP of the next step's subtile 0 follow the barrier
+    // that publishes its stage. Every wave takes every step (a fully masked subtile adds
+    // zeros), so the workgroup's waves stay in step between barriers.
     if (n_all > 0) {
         load_step(0);
         store_step(smem);
     }
+    // Settle every outstanding load (the K, V fragments included) so that no wait on them is
+    // left inside the loop; then start the loads of step 1.
     __builtin_amdgcn_s_waitcnt(0);
+    if (n_all > 1) load_step(1);
     __syncthreads();
+    f32x16 sA, dA, sB, dB;
+    int hq_unused;
+    int r_cur = N;
+    if (n_all > 0) {
+        r_cur = step_row(0, hq_unused);
+        sdp(smem, 0, sA, dA);
+    }
     int cur = 0;
-    for (int t = 0; t < n_all; ++t) {
-        const bool has_next = t + 1 < n_all;
-        if (has_next) load_step(t + 1);
-
+    int t = 0;
+    auto iterate = [&](bool mask) {
         const uint16_t* s = smem + cur * L::STAGE;
-        const float* sL = reinterpret_cast<const float*>(s + L::STATS);
-        const float* sDel = sL + kStep;
-        const uint16_t* qt_base = tr_lane_base(s + L::QT, C::TS, lane);
-        const uint16_t* dt_base = tr_lane_base(s + L::DT, C::TS, lane);
-        int hq_unused;
-        const int qt0 = step_row(t, hq_unused);
-        if (qt0 >= 0 && kw0 < N && (!CAUSAL || qt0 + kStep - 1 >= kw0)) {
+        uint16_t* s_next = smem + (cur ^ 1) * L::STAGE;
+        {
+            bf16x8 pa[2], da[2], pb[2], db[2];
+            sdp(s, 1, sB, dB);
+            probs(mask, s, 0, r_cur, sA, dA, pa, da);
+            grads(s, 0, pa, da);
+            probs(mask, s, 1, r_cur, sB, dB, pb, db);
+            grads(s, 1, pb, db);
+            // Issue order: one wave issues in order, so an MFMA run followed by a VALU run would
+            // not overlap, and an LDS read right before its MFMA exposes the read latency.
+            // Alternate each MFMA with about ten VALU operations of the other subtile's
+            // probabilities, and issue LDS reads several MFMAs ahead of their use:
+            // S, dP of subtile 1 beside subtile 0's probabilities; the gradient products of
+            // subtile 0 beside subtile 1's probabilities; then subtile 1's gradient products.
+            __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);          // LDS: stats, first rows
 #pragma unroll
-            for (int qb = 0; qb < kStep / 32; ++qb) {
-                if (CAUSAL && qt0 + 32 * qb + 31 < kw0) continue;   // every query before every key
-                // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys.
-                f32x16 sacc = {}, pacc = {};
-                const uint16_t* qr = s + L::QR + (32 * qb + i) * C::RS + 8 * hf;
-                const uint16_t* dr = s + L::DR + (32 * qb + i) * C::RS + 8 * hf;
+            for (int k = 0; k < 2 * KSTEPS; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+                if (k < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);      // VALU
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
 #pragma unroll
-                for (int ks = 0; ks < KSTEPS; ++ks) {
-                    sacc = mfma32(*reinterpret_cast<const bf16x8*>(qr + 16 * ks), kf[ks], sacc);
-                    pacc = mfma32(*reinterpret_cast<const bf16x8*>(dr + 16 * ks), vf[ks], pacc);
-                }
-                // Element r of this lane is query 32*qb + 8*(r/4) + 4*hf + r%4.
-                const bool masked = CAUSAL && qt0 + 32 * qb < kw0 + 31;
-                float lq[16], dq[16];
+            for (int k = 0; k < 4 * CB; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (k < 3 * CB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + 32 * qb + 8 * g + 4 * hf);
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(sDel + 32 * qb + 8 * g + 4 * hf);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        lq[4 * g + e] = l4[e];
-                        dq[4 * g + e] = d4[e];
-                    }
-                }
-                float pv[16], dsv[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float pe = fast_exp2(fmaf(sacc[r], c, -lq[r]));
-                    if (masked && key > qt0 + 32 * qb + acc_row(r, hf)) pe = 0.0f;
-                    pv[r] = pe;
-                    dsv[r] = pe * (pacc[r] - dq[r]);
-                }
-                bf16x8 pb[2], db[2];
-#pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    pb[st] = pack8(pv[8 * st], pv[8 * st + 1], pv[8 * st + 2], pv[8 * st + 3], pv[8 * st + 4],
-                                   pv[8 * st + 5], pv[8 * st + 6], pv[8 * st + 7]);
-                    db[st] = pack8(dsv[8 * st], dsv[8 * st + 1], dsv[8 * st + 2], dsv[8 * st + 3], dsv[8 * st + 4],
-                                   dsv[8 * st + 5], dsv[8 * st + 6], dsv[8 * st + 7]);
-                }
-                // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries.
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                    for (int st = 0; st < 2; ++st) {
-                        const int off = (32 * qb + 16 * st) * C::TS + 32 * cb;
-                        dv[cb] = mfma32(read_tr_operand(dt_base, off, C::TS), pb[st], dv[cb]);
-                        dk[cb] = mfma32(read_tr_operand(qt_base, off, C::TS), db[st], dk[cb]);
-                    }
+            for (int k = 0; k < 4 * CB; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (k < 3 * CB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
         }
-        if (has_next) store_step(smem + (cur ^ 1) * L::STAGE);
+        if (t + 1 < n_all) store_step(s_next);
         __syncthreads();
+        if (t + 2 < n_all) load_step(t + 2);
+        if (t + 1 < n_all) {
+            r_cur = step_row(t + 1, hq_unused);
+            sdp(s_next, 0, sA, dA);
+        }
         cur ^= 1;
-    }
+    };
+    for (; t < n_mask; ++t) iterate(true);
+    for (; t < n_all; ++t) iterate(false);
 
     if (key < N) {
         uint16_t* dkr = p.dk + seq_off(sp, b, hk, p.dksb, p.dksh, p.dksn) + (int64_t)key * p.dksn;
