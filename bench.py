@@ -3,8 +3,8 @@
 Headline (`value`): causal bf16 forward, B=1 H=32 N=32768 d=128 (the 32K x 128 case),
 one step = one fa_fwd call over inputs already resident in HBM. The other workloads
 (small dense head, 7B-like causal layer in (B,N,H,d), 128K block-sparse, causal
-backward; grouped K/V heads, packed variable-length sequences, block-sparse backward)
-are timed in the same run and reported under "workloads".
+backward; grouped K/V heads, packed variable-length sequences, block-sparse backward,
+fp8 inputs) are timed in the same run and reported under "workloads".
 
 FLOP conventions: forward 4*B*H*N^2*d, halved for causal; backward 2.5x the forward
 (five matrix products against two); block-sparse: listed 128x128 tiles x 4*128*128*d
@@ -82,6 +82,7 @@ def sparse_flops(w, offsets, indices) -> tuple[float, float]:
 
 def algorithmic_bytes(w, direction: str, nnz: int = 0) -> int:
     rows = w.total                              # B*N, or the packed row count
+    es = 1 if w.dtype == "fp8_e4m3" else 2      # bytes per input element (O is always bf16)
     tq = rows * w.H * w.d * 2                   # one bf16 tensor with the query heads
     tk = rows * w.hkv * w.d * 2                 # one bf16 tensor with the K/V heads
     lse = rows * w.H * 4
@@ -89,7 +90,7 @@ def algorithmic_bytes(w, direction: str, nnz: int = 0) -> int:
     if direction in ("bwd", "sparse_bwd"):
         # q k v o do read, dq dk dv written, lse read (+ both list forms)
         return 4 * tq + 4 * tk + lse + (2 * lists if w.sparse else 0)
-    return 2 * tq + 2 * tk + lse + lists        # q k v read, o written, lse written
+    return (tq + 2 * tk) * es // 2 + tq + lse + lists   # q k v read, o written, lse written
 
 
 def len_off(w) -> int:
@@ -125,11 +126,13 @@ def prepare(fa, W, torch, key):
     w = W.WORKLOADS[key]
     log(f"[bench] preparing {key}: {w.describe()}")
     x = W.make_inputs(w)
-    dev = {n: t.to("cuda") for n, t in x.items()}
+    dev = {n: t.to("cuda") for n, t in x.items() if hasattr(t, "to")}
     info = dict(workload=w, x=x, dev=dev)
-    # grouped heads and packed sequences go through the general entry points
-    general = w.packed or w.hkv != w.H
+    # grouped heads, packed sequences and fp8 inputs go through the general entry points
+    general = w.packed or w.hkv != w.H or w.dtype != "bf16"
     kw = dict(causal=w.causal, scale=w.scale)
+    if w.dtype != "bf16":
+        kw.update(q_descale=x["q_descale"], k_descale=x["k_descale"], v_descale=x["v_descale"])
     if w.packed:
         kw.update(cu_seqlens=torch.from_numpy(w.cu_seqlens()).to("cuda"), max_seqlen=w.N)
     if w.direction == "fwd":

@@ -30,7 +30,8 @@ class AttnDesc(ctypes.Structure):
                 ("d", ctypes.c_int64), ("causal", ctypes.c_int), ("scale", ctypes.c_float),
                 ("cu_seqlens", ctypes.c_void_p), ("total", ctypes.c_int64), ("block_size", ctypes.c_int64),
                 ("kv_offsets", ctypes.c_void_p), ("kv_indices", ctypes.c_void_p), ("nnz", ctypes.c_int64),
-                ("q_offsets", ctypes.c_void_p), ("q_indices", ctypes.c_void_p)]
+                ("q_offsets", ctypes.c_void_p), ("q_indices", ctypes.c_void_p), ("dtype", ctypes.c_int),
+                ("q_descale", ctypes.c_float), ("k_descale", ctypes.c_float), ("v_descale", ctypes.c_float)]
 
 
 class FaError(RuntimeError):

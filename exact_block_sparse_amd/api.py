@@ -43,16 +43,17 @@ def _check_inputs(*ts: torch.Tensor) -> None:
             raise ValueError(f"shape mismatch {tuple(t.shape)} vs {tuple(ts[0].shape)}")
 
 
-def _empty_like_layout(t: torch.Tensor) -> torch.Tensor:
+def _empty_like_layout(t: torch.Tensor, dtype=None) -> torch.Tensor:
     """An uninitialised tensor with t's shape and, if t is a permuted dense tensor, its layout."""
+    dtype = t.dtype if dtype is None else dtype
     order = sorted(range(t.dim()), key=lambda i: (-t.stride(i), i))
     p = t.permute(*order)
     if p.is_contiguous():
         inv = [0] * t.dim()
         for j, i in enumerate(order):
             inv[i] = j
-        return torch.empty(p.shape, dtype=t.dtype, device=t.device).permute(*inv)
-    return torch.empty(t.shape, dtype=t.dtype, device=t.device)
+        return torch.empty(p.shape, dtype=dtype, device=t.device).permute(*inv)
+    return torch.empty(t.shape, dtype=dtype, device=t.device)
 
 
 def _stream(dev: torch.device):
@@ -196,10 +197,15 @@ def _packed_strides(t: torch.Tensor) -> Strides:
     return Strides(0, t.stride(1), t.stride(0))
 
 
-def _check_group(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, packed: bool) -> None:
+FP8 = getattr(torch, "float8_e4m3fn", None)
+
+
+def _check_group(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, packed: bool, allow_fp8: bool = False) -> None:
     for t in (q, k, v):
-        if t.dtype != torch.bfloat16:
-            raise TypeError(f"expected bfloat16 tensors, got {t.dtype}")
+        ok = t.dtype == torch.bfloat16 or (allow_fp8 and FP8 is not None and t.dtype == FP8)
+        if not ok or t.dtype != q.dtype:
+            raise TypeError(f"expected bfloat16{' or float8_e4m3fn' if allow_fp8 else ''} tensors of one dtype, "
+                            f"got {q.dtype}, {k.dtype}, {v.dtype}")
         if t.device.type != "cuda" or t.device != q.device:
             raise ValueError("tensors must be on one GPU device")
     hd = 1
@@ -210,10 +216,13 @@ def _check_group(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, packed: bool
         raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} differ outside the head axis")
 
 
-def _desc(B, H, H_kv, N, d, causal, scale, cu=None, total=0, lists=None) -> AttnDesc:
+def _desc(B, H, H_kv, N, d, causal, scale, cu=None, total=0, lists=None, fp8=False,
+          descales=(1.0, 1.0, 1.0)) -> AttnDesc:
     x = AttnDesc()
     x.B, x.H, x.H_kv, x.N, x.d = B, H, H_kv, N, d
     x.causal, x.scale = int(bool(causal)), float(scale)
+    x.dtype = 1 if fp8 else 0
+    x.q_descale, x.k_descale, x.v_descale = (float(s) for s in descales)
     x.cu_seqlens = cu.data_ptr() if cu is not None else None
     x.total = int(total)
     if lists is not None:
@@ -268,16 +277,19 @@ def _device_lists(kv_offsets, kv_indices, q_offsets, q_indices, n_blocks, causal
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
              scale: float | None = None, cu_seqlens=None, max_seqlen: int | None = None,
              kv_offsets=None, kv_indices=None, block_size: int = BLOCK,
-             out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
-    """General forward through ``fa_attn_fwd``: grouped K/V heads, packed sequences, block lists.
+             out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+             q_descale: float = 1.0, k_descale: float = 1.0, v_descale: float = 1.0):
+    """General forward through ``fa_attn_fwd``: grouped K/V heads, packed sequences, block lists,
+    bf16 or fp8 (``torch.float8_e4m3fn``, real value = code x descale) inputs.
 
-    Fixed length: q [B, H, N, d], k and v [B, H_kv, N, d]; returns O like q and LSE [B, H, N].
-    Packed (``cu_seqlens`` given, int32 [B+1], host or device): q [total, H, d], k and v
-    [total, H_kv, d]; returns O like q and LSE [H, total]. ``max_seqlen`` bounds every
+    Fixed length: q [B, H, N, d], k and v [B, H_kv, N, d]; returns O (bf16) in q's layout and
+    LSE [B, H, N]. Packed (``cu_seqlens`` given, int32 [B+1], host or device): q [total, H, d],
+    k and v [total, H_kv, d]; returns O like q and LSE [H, total]. ``max_seqlen`` bounds every
     sequence's length (computed from host offsets when omitted).
     """
     packed = cu_seqlens is not None
-    _check_group(q, k, v, packed)
+    _check_group(q, k, v, packed, allow_fp8=True)
+    fp8 = q.dtype != torch.bfloat16
     d = q.shape[-1]
     H, H_kv = (q.shape[1], k.shape[1])
     pk, B, N, total, cu = _seq_args(q, cu_seqlens, max_seqlen)
@@ -285,11 +297,15 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool 
     if kv_offsets is not None:
         nb = (N + block_size - 1) // block_size
         lists = _device_lists(kv_offsets, kv_indices, None, None, nb, causal, block_size, q.device, False)
-    o = _empty_like_layout(q) if (out is None and not pk) else (torch.empty_like(q) if out is None else out)
+    if out is None:
+        o = _empty_like_layout(q, torch.bfloat16) if not pk else torch.empty(q.shape, dtype=torch.bfloat16,
+                                                                              device=q.device)
+    else:
+        o = out
     lshape = (H, total) if pk else (B, H, N)
     l = torch.empty(lshape, dtype=torch.float32, device=q.device) if lse is None else lse
     S = _packed_strides if pk else _strides
-    x = _desc(B, H, H_kv, N, d, causal, _scale(scale, d), cu, total, lists)
+    x = _desc(B, H, H_kv, N, d, causal, _scale(scale, d), cu, total, lists, fp8, (q_descale, k_descale, v_descale))
     with torch.cuda.device(q.device):
         st = lib.fa_attn_fwd(ctypes.byref(x), _ptr(q), S(q), _ptr(k), S(k), _ptr(v), S(v), _ptr(o), S(o), _ptr(l),
                              _stream(q.device))

@@ -46,12 +46,14 @@ int check_sizes(int64_t B, int64_t H, int64_t N, int64_t d) {
     return FA_OK;
 }
 
-int check_tensor(const char* name, const void* p, const fa_strides& s) {
+// Pointer and strides of one tensor; `mult` is the element count of 16 bytes (8 for bf16,
+// 16 for fp8), so that every row starts 16-byte aligned.
+int check_tensor(const char* name, const void* p, const fa_strides& s, int mult = 8) {
     if (!p) return fail(FA_ERR_NULL, "%s is NULL", name);
     if (!aligned16(p)) return fail(FA_ERR_LAYOUT, "%s is not 16-byte aligned", name);
-    if ((s.b % 8) || (s.h % 8) || (s.n % 8))
-        return fail(FA_ERR_LAYOUT, "%s strides (%lld, %lld, %lld) are not multiples of 8 elements", name,
-                    (long long)s.b, (long long)s.h, (long long)s.n);
+    if ((s.b % mult) || (s.h % mult) || (s.n % mult))
+        return fail(FA_ERR_LAYOUT, "%s strides (%lld, %lld, %lld) are not multiples of %d elements", name,
+                    (long long)s.b, (long long)s.h, (long long)s.n, mult);
     if (s.b < 0 || s.h < 0 || s.n < 0) return fail(FA_ERR_LAYOUT, "%s has a negative stride", name);
     return FA_OK;
 }
@@ -92,6 +94,14 @@ int check_desc(const fa_attn_desc* dp, bool backward) {
     if (packed(d) && d.total * d.H > kMaxDim)
         return fail(FA_ERR_SHAPE, "H * total too large (%lld * %lld)", (long long)d.H, (long long)d.total);
     if (!std::isfinite(d.scale)) return fail(FA_ERR_ARG, "scale is not finite");
+    if (d.dtype != FA_DTYPE_BF16 && d.dtype != FA_DTYPE_FP8_E4M3) return fail(FA_ERR_ARG, "unknown dtype %d", d.dtype);
+    if (d.dtype == FA_DTYPE_FP8_E4M3) {
+        if (backward) return fail(FA_ERR_ARG, "the backward takes bf16 tensors only");
+        if (!std::isfinite(d.q_descale) || !std::isfinite(d.k_descale) || !std::isfinite(d.v_descale))
+            return fail(FA_ERR_ARG, "a descale is not finite");
+        if (!std::isfinite(d.scale * d.q_descale * d.k_descale))
+            return fail(FA_ERR_ARG, "scale * q_descale * k_descale overflows");
+    }
     if (!d.kv_offsets && (d.kv_indices || d.q_offsets || d.q_indices))
         return fail(FA_ERR_NULL, "block lists given without kv_offsets");
     if (d.kv_offsets) {
@@ -142,11 +152,16 @@ int fa_attn_fwd(const fa_attn_desc* desc, const void* q, fa_strides sq, const vo
     if (st) return st;
     const fa_attn_desc& d = *desc;
     if (empty_problem(d)) return ok();
-    if ((st = check_tensor("q", q, sq)) || (st = check_tensor("k", k, sk)) || (st = check_tensor("v", v, sv)) ||
-        (st = check_tensor("o", o, so)) || (st = check_lse(lse)))
+    const bool f8 = d.dtype == FA_DTYPE_FP8_E4M3;
+    const int m = f8 ? 16 : 8;
+    if ((st = check_tensor("q", q, sq, m)) || (st = check_tensor("k", k, sk, m)) ||
+        (st = check_tensor("v", v, sv, m)) || (st = check_tensor("o", o, so)) || (st = check_lse(lse)))
         return st;
     if ((st = check_device())) return st;
     fa::FwdArgs a;
+    a.f8 = f8;
+    a.qk_desc = f8 ? d.q_descale * d.k_descale : 1.0f;
+    a.v_desc = f8 ? d.v_descale : 1.0f;
     a.L = layout(d);
     a.q = view(q, sq);
     a.k = view(k, sk);

@@ -103,13 +103,49 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
-// Bytes of rows [r0, n) of a matrix with row stride `sn` elements and `d` bf16 columns,
-// capped to `rows` rows; the cap keeps the value well inside 32 bits.
-__device__ __forceinline__ uint32_t rows_bytes(int r0, int n, int64_t sn, int d, int rows) {
+// Bytes of rows [r0, n) of a matrix with row stride `sn` elements and `d` columns of `es`
+// bytes (2: bf16, 1: fp8), capped to `rows` rows; the cap keeps the value well inside 32 bits.
+__device__ __forceinline__ uint32_t rows_bytes(int r0, int n, int64_t sn, int d, int rows, int es = 2) {
     int last = n - 1 - r0;
     if (last >= rows) last = rows - 1;
     if (last < 0) return 0u;
-    return (uint32_t)(((int64_t)last * sn + d) * 2);
+    return (uint32_t)(((int64_t)last * sn + d) * es);
+}
+
+// 16-byte global load from a byte address that yields zeros when `ok` is false.
+__device__ __forceinline__ u32x4 load16b(const uint8_t* p, bool ok) {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    return ok ? *reinterpret_cast<const u32x4*>(p) : z;
+}
+
+// fp8 (OCP e4m3) operands: 32 values per lane. D(32x32 fp32) += A(32x64) * B(64x32) with
+// v_mfma_f32_32x32x64_f8f6f4, twice the bf16 rate. Operand layout (measured): lane l supplies
+// row (A) / column (B) l % 32 and the 32 consecutive k-values 32*(l/32) .. 32*(l/32)+31; the
+// accumulator layout is the one of mfma32.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16 mfma32_f8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ i32x8 join8(const u32x4& lo, const u32x4& hi) {
+    i32x8 r;
+    r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
+    r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
+    return r;
+}
+// Sixteen fp8 (e4m3) values to sixteen bf16, exactly (every e4m3 value is a bf16 value):
+// word w of `x` holds values 4w .. 4w+3; the result's word j holds values 2j, 2j+1.
+__device__ __forceinline__ void fp8x16_to_bf16(const u32x4& x, u32x4& lo, u32x4& hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    uint32_t out[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, false);
+        const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, true);
+        out[2 * w] = __builtin_bit_cast(uint32_t, a);
+        out[2 * w + 1] = __builtin_bit_cast(uint32_t, b);
+    }
+    lo[0] = out[0]; lo[1] = out[1]; lo[2] = out[2]; lo[3] = out[3];
+    hi[0] = out[4]; hi[1] = out[5]; hi[2] = out[6]; hi[3] = out[7];
 }
 
 // Where one sequence lives. Fixed length (cu == nullptr): sequence b is the b-th [N, d]

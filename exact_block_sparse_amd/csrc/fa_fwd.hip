@@ -44,23 +44,28 @@ constexpr int kBK = 64;            // keys per pipeline step
 constexpr int kSparseBlock = 128;
 constexpr float kRescaleSlack = 8.0f;   // log2 of the largest probability allowed before a rescale
 
-template <int D>
+template <int D, bool F8 = false>
 struct Cfg {
-    static constexpr int KS = D + 8;             // K tile row stride in LDS (elements)
-    static constexpr int VS = D + 32;            // V tile row stride in LDS (elements)
+    // K tile row stride: bf16 rows of D elements padded to D + 8 (272 bytes at D = 128), or
+    // fp8 rows of D bytes padded by 16 (144 bytes): both keep 16-byte row reads conflict-free.
+    static constexpr int KROWB = F8 ? D + 16 : 2 * (D + 8);
+    static constexpr int KS = KROWB / 2;         // K tile row stride in LDS (uint16 units)
+    static constexpr int VS = D + 32;            // V tile row stride in LDS (bf16 elements)
     static constexpr int KEL = kBK * KS;
     static constexpr int VEL = kBK * VS;
     static constexpr int BUF = KEL + VEL;        // elements per pipeline stage
     static constexpr int CR = D / 8;             // 16-byte chunks per row
-    static constexpr int KSTEPS = D / 16;        // MFMA k-steps over the head dimension
+    static constexpr int KSTEPS = D / 16;        // MFMA k-steps over the head dimension (bf16)
+    static constexpr int KSTEPS8 = D / 64;       // ... with fp8 operands
+    static constexpr int CR8 = D / 16;           // 16-byte chunks per fp8 row
     static constexpr int CB = D / 32;            // 32-wide head-dimension blocks of O
     static_assert((BUF * 2) % 16 == 0, "stage size must keep 16-byte alignment");
 };
 
 struct Params {
-    const uint16_t* q;
-    const uint16_t* k;
-    const uint16_t* v;
+    const void* q;    // bf16 or fp8 (e4m3) elements
+    const void* k;
+    const void* v;
     uint16_t* o;
     float* lse;
     int64_t qsb, qsh, qsn, ksb, ksh, ksn, vsb, vsh, vsn, osb, osh, osn;
@@ -69,7 +74,8 @@ struct Params {
     const int32_t* cu;   // packed sequence offsets [B + 1], or nullptr
     int64_t total;       // packed rows
     int nqb;          // query blocks (of the workgroup's row count) per head
-    float c;          // scale * log2(e)
+    float c;          // scale * log2(e) (fp8: times the Q and K descales)
+    float vdesc;      // V descale (fp8), 1 for bf16
     const int32_t* kv_offsets;
     const int32_t* kv_indices;
     int64_t nnz;
@@ -115,11 +121,73 @@ struct Stage {
     }
 };
 
+// Per-thread staging of one K/V step from fp8 (e4m3) tensors: 16-byte row chunks. K stays
+// fp8 in LDS (the scores run on the fp8 MFMA); V is widened to bf16 on its way to LDS (an
+// exact conversion) so that P.V is the bf16 product of the bf16 path.
+template <int D, int NT>
+struct Stage8 {
+    using C = Cfg<D, true>;
+    static constexpr int TOT = kBK * C::CR8;           // chunks per tile and tensor
+    static constexpr int CH = (TOT + NT - 1) / NT;
+    static_assert(TOT % NT == 0 || NT % TOT == 0, "chunks must divide evenly");
+    u32x4 k[CH];
+    u32x4 v[CH];
+    uint32_t koff[CH], voff[CH];
+    int klds[CH], vlds[CH];
+    bool ok[CH];
+
+    __device__ void init(int tid, int64_t ksn, int64_t vsn) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int id = tid + j * NT;
+            ok[j] = id < TOT;
+            const int row = (id % TOT) / C::CR8, ch = id % C::CR8;
+            koff[j] = (uint32_t)((int64_t)row * ksn + 16 * ch);
+            voff[j] = (uint32_t)((int64_t)row * vsn + 16 * ch);
+            klds[j] = row * C::KS + 8 * ch;
+            vlds[j] = C::KEL + row * C::VS + 16 * ch;
+        }
+    }
+    __device__ void load(const uint8_t* kbase, const uint8_t* vbase, int64_t ksn, int64_t vsn, int kt0, int N) {
+        const auto kr = make_rsrc(kbase + (int64_t)kt0 * ksn, rows_bytes(kt0, N, ksn, D, kBK, 1));
+        const auto vr = make_rsrc(vbase + (int64_t)kt0 * vsn, rows_bytes(kt0, N, vsn, D, kBK, 1));
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+            if (ok[j]) k[j] = buf_load16(kr, koff[j], 0);
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+            if (ok[j]) v[j] = buf_load16(vr, voff[j], 0);
+    }
+    __device__ void store(uint16_t* buf) const {
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+            if (ok[j]) *reinterpret_cast<u32x4*>(buf + klds[j]) = k[j];
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+            if (ok[j]) {
+                u32x4 lo, hi;
+                fp8x16_to_bf16(v[j], lo, hi);
+                *reinterpret_cast<u32x4*>(buf + vlds[j]) = lo;
+                *reinterpret_cast<u32x4*>(buf + vlds[j] + 8) = hi;
+            }
+    }
+};
+
+template <int D, int NT, bool F8> struct StageOf { using type = Stage<D, NT>; };
+template <int D, int NT> struct StageOf<D, NT, true> { using type = Stage8<D, NT>; };
+template <bool F8> struct ElemOf { using type = uint16_t; };
+template <> struct ElemOf<true> { using type = uint8_t; };
+
+// Q rows as MFMA B operands (column = query, k-group = half): bf16, 8 values per 16-wide
+// k-step, or fp8, 32 values per 64-wide k-step.
+template <int D, bool F8> struct QFrag { bf16x8 v[D / 16]; };
+template <int D> struct QFrag<D, true> { i32x8 v[D / 64]; };
+
 // Per-wave state of 32 query rows.
-template <int D>
+template <int D, bool F8>
 struct Rows {
-    using C = Cfg<D>;
-    bf16x8 qf[C::KSTEPS];   // Q rows as B operands (column = query, k-group = half)
+    using C = Cfg<D, F8>;
+    QFrag<D, F8> qf;        // Q rows as B operands
     f32x16 o[C::CB];        // O^T accumulators
     float m_run, l_part;    // running max (exp2 domain) and this lane's partial row sum
     f32x16 s[2];            // scores of the current 64-key step (two 32-key blocks)
@@ -127,25 +195,38 @@ struct Rows {
 };
 
 // S^T = K Q^T for one 64-key step. Row i of each 32-key block; the two blocks' chains alternate.
-template <int D>
-__device__ __forceinline__ void scores(const uint16_t* buf, Rows<D>& w, int i, int hf) {
-    using C = Cfg<D>;
+template <int D, bool F8>
+__device__ __forceinline__ void scores(const uint16_t* buf, Rows<D, F8>& w, int i, int hf) {
+    using C = Cfg<D, F8>;
     w.s[0] = f32x16{};
     w.s[1] = f32x16{};
-    const uint16_t* kr = buf + i * C::KS + 8 * hf;
+    if constexpr (!F8) {
+        const uint16_t* kr = buf + i * C::KS + 8 * hf;
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks)
+        for (int ks = 0; ks < C::KSTEPS; ++ks)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-            w.s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kr + 32 * kb * C::KS + 16 * ks), w.qf[ks], w.s[kb]);
+            for (int kb = 0; kb < 2; ++kb)
+                w.s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kr + 32 * kb * C::KS + 16 * ks), w.qf.v[ks], w.s[kb]);
+    } else {
+        // lane (key i, half hf) reads the 32 bytes 32*hf + 64*ks .. of its K row
+        const uint8_t* kr = reinterpret_cast<const uint8_t*>(buf) + i * C::KROWB + 32 * hf;
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS8; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const uint8_t* a = kr + 32 * kb * C::KROWB + 64 * ks;
+                w.s[kb] = mfma32_f8(join8(*reinterpret_cast<const u32x4*>(a), *reinterpret_cast<const u32x4*>(a + 16)),
+                                    w.qf.v[ks], w.s[kb]);
+            }
+    }
 }
 
 // Online softmax update for one step: mask (diagonal or tail tiles only), tile max, lazy
 // rescale, probabilities, fp32 row sum, bf16 operands. `masked` is uniform across the wave.
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void softmax(Rows<D>& w, bool masked, int kt0, int qrow, int N, float c, bool cpos,
+template <int D, bool F8, bool CAUSAL>
+__device__ __forceinline__ void softmax(Rows<D, F8>& w, bool masked, int kt0, int qrow, int N, float c, bool cpos,
                                         int hf) {
-    using C = Cfg<D>;
+    using C = Cfg<D, F8>;
     // In masked tiles the scores are scaled here and masked keys (past the sequence end,
     // or after the query under causal masking) become -inf; the exponent below then uses
     // a unit multiplier. Elsewhere the scale is folded into the exponent's FMA.
@@ -219,9 +300,9 @@ __device__ __forceinline__ void softmax(Rows<D>& w, bool masked, int kt0, int qr
 // k = key) comes from the row-major V tile through two transposing reads: lane j of each
 // 16-lane group addresses V[key0 + j/4][col0 + 4*(j%4)] and receives the 4 keys of column
 // col0 + j.
-template <int D>
-__device__ __forceinline__ void pv(const uint16_t* buf, Rows<D>& w, int i, int hf) {
-    using C = Cfg<D>;
+template <int D, bool F8>
+__device__ __forceinline__ void pv(const uint16_t* buf, Rows<D, F8>& w, int i, int hf) {
+    using C = Cfg<D, F8>;
     const int g16 = (i >> 4) & 1, j16 = i & 15;
     const uint16_t* vr = buf + C::KEL + (4 * hf + (j16 >> 2)) * C::VS + 16 * g16 + 4 * (j16 & 3);
 #pragma unroll
@@ -245,12 +326,21 @@ __device__ __forceinline__ void pv(const uint16_t* buf, Rows<D>& w, int i, int h
     }
 }
 
-template <int D>
-__device__ __forceinline__ void load_q(Rows<D>& w, const uint16_t* qp, int64_t qsn, int qrow, int N, int hf) {
-    using C = Cfg<D>;
+template <int D, bool F8>
+__device__ __forceinline__ void load_q(Rows<D, F8>& w, const typename ElemOf<F8>::type* qp, int64_t qsn, int qrow,
+                                       int N, int hf) {
+    using C = Cfg<D, F8>;
+    if constexpr (!F8) {
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks)
-        w.qf[ks] = as_bf16x8(load16(qp + (int64_t)qrow * qsn + 16 * ks + 8 * hf, qrow < N));
+        for (int ks = 0; ks < C::KSTEPS; ++ks)
+            w.qf.v[ks] = as_bf16x8(load16(qp + (int64_t)qrow * qsn + 16 * ks + 8 * hf, qrow < N));
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS8; ++ks) {
+            const uint8_t* a = qp + (int64_t)qrow * qsn + 64 * ks + 32 * hf;
+            w.qf.v[ks] = join8(load16b(a, qrow < N), load16b(a + 16, qrow < N));
+        }
+    }
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb) w.o[cb] = f32x16{};
     w.m_run = kNegInf;
@@ -259,13 +349,13 @@ __device__ __forceinline__ void load_q(Rows<D>& w, const uint16_t* qp, int64_t q
 
 // O = O^T / l as bf16; LSE = (m + log2 l) * ln 2. `obase` and `lbase` point at row 0 of the
 // sequence's head.
-template <int D>
-__device__ __forceinline__ void epilogue(const Rows<D>& w, uint16_t* obase, int64_t osn, float* lbase, int qrow,
-                                         int N, int hf) {
-    using C = Cfg<D>;
+template <int D, bool F8>
+__device__ __forceinline__ void epilogue(const Rows<D, F8>& w, uint16_t* obase, int64_t osn, float* lbase, int qrow,
+                                         int N, int hf, float vdesc) {
+    using C = Cfg<D, F8>;
     const float l_tot = pair_sum(w.l_part);
     if (qrow >= N) return;
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float inv = l_tot > 0.0f ? vdesc / l_tot : 0.0f;
     uint16_t* orow = obase + (int64_t)qrow * osn;
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb)
@@ -286,9 +376,10 @@ constexpr int kPPThreads = 512;   // 8 waves, two groups of four
 constexpr int kPPRows = 256;      // query rows per workgroup
 constexpr int kPPBufs = 3;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F8>
 __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_kernel(Params p) {
-    using C = Cfg<D>;
+    using C = Cfg<D, F8>;
+    using E = typename ElemOf<F8>::type;
     __shared__ __attribute__((aligned(16))) uint16_t smem[kPPBufs * C::BUF];
 
     const int tid = threadIdx.x;
@@ -306,15 +397,15 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_kernel(Params p) {
     if (q0 >= N) return;   // past the end of a shorter packed sequence (uniform per workgroup)
 
     const int hk = hh / p.G;
-    const uint16_t* kp = p.k + seq_off(sp, b, hk, p.ksb, p.ksh, p.ksn);
-    const uint16_t* vp = p.v + seq_off(sp, b, hk, p.vsb, p.vsh, p.vsn);
+    const E* kp = static_cast<const E*>(p.k) + seq_off(sp, b, hk, p.ksb, p.ksh, p.ksn);
+    const E* vp = static_cast<const E*>(p.v) + seq_off(sp, b, hk, p.vsb, p.vsh, p.vsn);
 
     const int qw0 = q0 + 32 * wave;
     const int qrow = qw0 + i;
     const int qlast = min(q0 + kPPRows - 1, N - 1);
 
-    Rows<D> w;
-    load_q<D>(w, p.q + seq_off(sp, b, hh, p.qsb, p.qsh, p.qsn), p.qsn, qrow, N, hf);
+    Rows<D, F8> w;
+    load_q<D, F8>(w, static_cast<const E*>(p.q) + seq_off(sp, b, hh, p.qsb, p.qsh, p.qsn), p.qsn, qrow, N, hf);
 
     int T = (N + kBK - 1) / kBK;
     if (CAUSAL) T = min(T, qlast / kBK + 1);
@@ -325,7 +416,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_kernel(Params p) {
     const float c = p.c;
     const bool cpos = c >= 0.0f;
 
-    Stage<D, kPPThreads> st;
+    typename StageOf<D, kPPThreads, F8>::type st;
     st.init(tid, p.ksn, p.vsn);
     if (T > 0) {
         st.load(kp, vp, p.ksn, p.vsn, 0, N);
@@ -352,26 +443,27 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_kernel(Params p) {
         if (lp >= 0 && rows_valid) {
             const int t = lp >> 1;
             if ((lp & 1) == 0) {
-                if (t >= 1 && t - 1 < Tw) pv<D>(smem + ((t - 1) % kPPBufs) * C::BUF, w, i, hf);
-                if (t < Tw) scores<D>(smem + (t % kPPBufs) * C::BUF, w, i, hf);
+                if (t >= 1 && t - 1 < Tw) pv<D, F8>(smem + ((t - 1) % kPPBufs) * C::BUF, w, i, hf);
+                if (t < Tw) scores<D, F8>(smem + (t % kPPBufs) * C::BUF, w, i, hf);
             } else if (t < Tw) {
                 const int kt = t * kBK;
                 const bool masked = (kt + kBK > N) || (CAUSAL && kt + kBK - 1 > qw0);
-                softmax<D, CAUSAL>(w, masked, kt, qrow, N, c, cpos, hf);
+                softmax<D, F8, CAUSAL>(w, masked, kt, qrow, N, c, cpos, hf);
             }
         }
         __syncthreads();
     }
-    epilogue<D>(w, p.o + seq_off(sp, b, hh, p.osb, p.osh, p.osn), p.osn,
-                p.lse + seq_stat_off(sp, b, hh, p.H, p.N, p.total), qrow, N, hf);
+    epilogue<D, F8>(w, p.o + seq_off(sp, b, hh, p.osb, p.osh, p.osn), p.osn,
+                    p.lse + seq_stat_off(sp, b, hh, p.H, p.N, p.total), qrow, N, hf, p.vdesc);
 }
 
 // ----------------------------------------------------------------------------- sparse
 constexpr int kSpThreads = 256;   // 4 waves, one 128-row block
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F8>
 __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
-    using C = Cfg<D>;
+    using C = Cfg<D, F8>;
+    using E = typename ElemOf<F8>::type;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
 
     const int tid = threadIdx.x;
@@ -387,15 +479,15 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
     if (q0 >= N) return;   // past the end of a shorter packed sequence (uniform per workgroup)
 
     const int hk = hh / p.G;
-    const uint16_t* kp = p.k + seq_off(sp, b, hk, p.ksb, p.ksh, p.ksn);
-    const uint16_t* vp = p.v + seq_off(sp, b, hk, p.vsb, p.vsh, p.vsn);
+    const E* kp = static_cast<const E*>(p.k) + seq_off(sp, b, hk, p.ksb, p.ksh, p.ksn);
+    const E* vp = static_cast<const E*>(p.v) + seq_off(sp, b, hk, p.vsb, p.vsh, p.vsn);
 
     const int qw0 = q0 + 32 * wave;
     const int qrow = qw0 + i;
     const int qlast = min(q0 + kSparseBlock - 1, N - 1);
 
-    Rows<D> w;
-    load_q<D>(w, p.q + seq_off(sp, b, hh, p.qsb, p.qsh, p.qsn), p.qsn, qrow, N, hf);
+    Rows<D, F8> w;
+    load_q<D, F8>(w, static_cast<const E*>(p.q) + seq_off(sp, b, hh, p.qsb, p.qsh, p.qsn), p.qsn, qrow, N, hf);
 
     // Step t covers half (t & 1) of the listed key block kv_indices[t >> 1]. Offsets are
     // clamped to [0, nnz]; out-of-range and (causal) above-diagonal entries are skipped.
@@ -418,7 +510,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
     const float c = p.c;
     const bool cpos = c >= 0.0f;
 
-    Stage<D, kSpThreads> st;
+    typename StageOf<D, kSpThreads, F8>::type st;
     st.init(tid, p.ksn, p.vsn);
     if (t < t_end) {
         st.load(kp, vp, p.ksn, p.vsn, kt, N);
@@ -439,9 +531,9 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
         const uint16_t* buf = smem + cur * C::BUF;
         if (qw0 < N && (!CAUSAL || kt <= qw0 + 31)) {
             const bool masked = (kt + kBK > N) || (CAUSAL && kt + kBK - 1 > qw0);
-            scores<D>(buf, w, i, hf);
-            softmax<D, CAUSAL>(w, masked, kt, qrow, N, c, cpos, hf);
-            pv<D>(buf, w, i, hf);
+            scores<D, F8>(buf, w, i, hf);
+            softmax<D, F8, CAUSAL>(w, masked, kt, qrow, N, c, cpos, hf);
+            pv<D, F8>(buf, w, i, hf);
         }
         if (has_next) st.store(smem + (cur ^ 1) * C::BUF);
         __syncthreads();
@@ -449,37 +541,37 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
         t = tn;
         kt = ktn;
     }
-    epilogue<D>(w, p.o + seq_off(sp, b, hh, p.osb, p.osh, p.osn), p.osn,
-                p.lse + seq_stat_off(sp, b, hh, p.H, p.N, p.total), qrow, N, hf);
+    epilogue<D, F8>(w, p.o + seq_off(sp, b, hh, p.osb, p.osh, p.osn), p.osn,
+                    p.lse + seq_stat_off(sp, b, hh, p.H, p.N, p.total), qrow, N, hf, p.vdesc);
 }
 
-template <int D>
-hipError_t dispatch(Params p, bool causal, bool sparse, hipStream_t stream) {
+template <int D, bool CAUSAL, bool F8>
+hipError_t dispatch(Params p, bool sparse, hipStream_t stream) {
     if (sparse) {
         p.nqb = (p.N + kSparseBlock - 1) / kSparseBlock;
         const int64_t grid = (int64_t)p.B * p.H * p.nqb;
-        if (causal)
-            hipLaunchKernelGGL((fwd_sparse_kernel<D, true>), dim3((unsigned)grid), dim3(kSpThreads), 0, stream, p);
-        else
-            hipLaunchKernelGGL((fwd_sparse_kernel<D, false>), dim3((unsigned)grid), dim3(kSpThreads), 0, stream, p);
+        hipLaunchKernelGGL((fwd_sparse_kernel<D, CAUSAL, F8>), dim3((unsigned)grid), dim3(kSpThreads), 0, stream, p);
         return hipGetLastError();
     }
     p.nqb = (p.N + kPPRows - 1) / kPPRows;
     const int64_t grid = (int64_t)p.B * p.H * p.nqb;
-    if (causal)
-        hipLaunchKernelGGL((fwd_pingpong_kernel<D, true>), dim3((unsigned)grid), dim3(kPPThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL((fwd_pingpong_kernel<D, false>), dim3((unsigned)grid), dim3(kPPThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_pingpong_kernel<D, CAUSAL, F8>), dim3((unsigned)grid), dim3(kPPThreads), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch_d(Params p, bool causal, bool sparse, bool f8, hipStream_t stream) {
+    if (f8) return causal ? dispatch<D, true, true>(p, sparse, stream) : dispatch<D, false, true>(p, sparse, stream);
+    return causal ? dispatch<D, true, false>(p, sparse, stream) : dispatch<D, false, false>(p, sparse, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     Params p;
-    p.q = static_cast<const uint16_t*>(a.q.p);
-    p.k = static_cast<const uint16_t*>(a.k.p);
-    p.v = static_cast<const uint16_t*>(a.v.p);
+    p.q = a.q.p;
+    p.k = a.k.p;
+    p.v = a.v.p;
     p.o = static_cast<uint16_t*>(a.o);
     p.lse = a.lse;
     p.qsb = a.q.sb; p.qsh = a.q.sh; p.qsn = a.q.sn;
@@ -491,13 +583,14 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     p.cu = a.L.cu;
     p.total = a.L.total;
     p.nqb = 0;
-    p.c = a.scale * kLog2e;
+    p.c = a.scale * a.qk_desc * kLog2e;
+    p.vdesc = a.v_desc;
     p.kv_offsets = a.kv_offsets;
     p.kv_indices = a.kv_indices;
     p.nnz = a.nnz;
     const bool sparse = a.kv_offsets != nullptr;
-    if (a.L.d == 64) return dispatch<64>(p, a.causal != 0, sparse, stream);
-    return dispatch<128>(p, a.causal != 0, sparse, stream);
+    if (a.L.d == 64) return dispatch_d<64>(p, a.causal != 0, sparse, a.f8 != 0, stream);
+    return dispatch_d<128>(p, a.causal != 0, sparse, a.f8 != 0, stream);
 }
 
 }  // namespace fa

@@ -32,6 +32,11 @@ struct FwdArgs {
     float* lse;
     int causal;
     float scale;
+    // element type of q, k, v: bf16 (f8 == 0) or fp8 e4m3 (f8 != 0, real value = code x
+    // descale; the score descale qk_desc is the product of the Q and K descales)
+    int f8;
+    float qk_desc;
+    float v_desc;
     // block-sparse mode (kv_offsets != nullptr)
     const int32_t* kv_offsets;
     const int32_t* kv_indices;

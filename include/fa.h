@@ -58,6 +58,10 @@ extern "C" {
 #define FA_ERR_ARG 8        /* other invalid argument (scale not finite, bad rule, ...)     */
 #define FA_ERR_CAPACITY 9   /* a host output array is too small                             */
 
+/* Element types of q, k, v in fa_attn_desc.dtype. */
+#define FA_DTYPE_BF16 0      /* bfloat16 (every entry point)                                */
+#define FA_DTYPE_FP8_E4M3 1  /* OCP fp8 e4m3 with per-tensor descales (fa_attn_fwd only)    */
+
 /* Element strides of one [B, H, N, d] tensor; the d stride is 1. */
 typedef struct fa_strides {
     int64_t b;
@@ -181,6 +185,15 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, co
  * ascending query blocks whose lists name it, as produced by fa_transpose_block_lists.
  * With packed sequences the lists apply to every sequence, block numbers counted from the
  * sequence's first row; they must cover ceil(N / block_size) blocks.
+ *
+ * FP8 inputs (forward only; the page's FAQ on FP16 vs FP8 names FP8 attention). With
+ * dtype = FA_DTYPE_FP8_E4M3, q, k and v hold OCP e4m3 codes (1 byte, strides in bytes,
+ * multiples of 16) and each tensor's real values are code x descale (q_descale, k_descale,
+ * v_descale; finite). The scores Q K^T are computed on the fp8 matrix cores from the codes
+ * (exact products, fp32 accumulation) and scaled by scale * q_descale * k_descale; V is
+ * widened to bf16 exactly and P V runs as in the bf16 path, O is multiplied by v_descale.
+ * The result is exact attention over the dequantized inputs to the same rounding as the
+ * bf16 path: o stays bf16, lse fp32. The descales are ignored for bf16.
  */
 typedef struct fa_attn_desc {
     int64_t B;                  /* sequences (batch)                                          */
@@ -198,6 +211,10 @@ typedef struct fa_attn_desc {
     int64_t nnz;                /* entries of kv_indices (and of q_indices)                    */
     const int32_t* q_offsets;   /* backward, block-sparse: device int32 [nb + 1], key side     */
     const int32_t* q_indices;   /* device int32 [nnz]                                          */
+    int dtype;                  /* FA_DTYPE_BF16 or FA_DTYPE_FP8_E4M3 (forward only)           */
+    float q_descale;            /* fp8: real value = code x descale                           */
+    float k_descale;
+    float v_descale;
 } fa_attn_desc;
 
 /*
@@ -205,7 +222,9 @@ typedef struct fa_attn_desc {
  * fa_fwd, or of fa_sparse_fwd when kv_offsets != NULL, with grouped heads and packed
  * sequences as described there). q, o: H heads; k, v: H_kv heads. lse: fp32 [B, H, N]
  * contiguous, or [H, total] when packed. Errors as in fa_fwd and fa_sparse_fwd; FA_ERR_SHAPE
- * also for H not a multiple of H_kv or a bad total; FA_ERR_NULL for NULL desc.
+ * also for H not a multiple of H_kv or a bad total; FA_ERR_NULL for NULL desc; FA_ERR_ARG for
+ * an unknown dtype or a descale that is not finite; FA_ERR_LAYOUT for fp8 strides that are
+ * not multiples of 16 bytes.
  */
 FA_API int fa_attn_fwd(const fa_attn_desc* desc, const void* q, fa_strides sq, const void* k, fa_strides sk,
                        const void* v, fa_strides sv, void* o, fa_strides so, float* lse, void* stream);
@@ -223,7 +242,8 @@ FA_API size_t fa_attn_bwd_workspace_bytes(const fa_attn_desc* desc);
  * and block-sparse masks (kv_offsets / kv_indices for dQ, q_offsets / q_indices for dK and
  * dV; both describe the same pattern, which must be the one the forward used). o and lse
  * are the forward's outputs for the same desc. The kernels are deterministic (no atomics).
- * Errors as in fa_bwd; FA_ERR_NULL also when block-sparse and q_offsets is NULL.
+ * Errors as in fa_bwd; FA_ERR_NULL also when block-sparse and q_offsets is NULL; FA_ERR_ARG
+ * when dtype is not FA_DTYPE_BF16 (the backward is bf16).
  */
 FA_API int fa_attn_bwd(const fa_attn_desc* desc, const void* q, fa_strides sq, const void* k, fa_strides sk,
                        const void* v, fa_strides sv, const void* o, fa_strides so, const void* dout,

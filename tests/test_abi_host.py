@@ -181,9 +181,21 @@ def call_attn_bwd(fa, desc, ws=16, ws_bytes=1 << 30):
 
 
 def test_attn_desc_layout_matches_header(fa):
-    # int64 x5, int + float sharing one 8-byte slot, then 8-byte pointers and int64s: 14 slots
-    assert ctypes.sizeof(fa.AttnDesc) == 8 * 14
+    # int64 x5, int + float sharing one 8-byte slot, 8-byte pointers and int64s up to
+    # q_indices, then int dtype and three float descales
+    assert ctypes.sizeof(fa.AttnDesc) == 128
     assert fa.AttnDesc.cu_seqlens.offset == 48 and fa.AttnDesc.q_indices.offset == 104
+    assert fa.AttnDesc.dtype.offset == 112 and fa.AttnDesc.v_descale.offset == 124
+
+
+def test_fp8_argument_errors(fa):
+    ok = dict(dtype=1, q_descale=0.01, k_descale=0.02, v_descale=0.03)
+    assert call_attn_fwd(fa, make_desc(fa, dtype=2)) == 8                      # unknown dtype
+    assert call_attn_fwd(fa, make_desc(fa, **{**ok, "k_descale": float("inf")})) == 8
+    assert call_attn_fwd(fa, make_desc(fa, **ok), st=(8192, 8192, 136)) == 4   # fp8 rows need 16-byte strides
+    assert call_attn_bwd(fa, make_desc(fa, **ok)) == 8                         # backward is bf16 only
+    assert "bf16" in fa.lib.fa_last_error().decode()
+    assert call_attn_fwd(fa, make_desc(fa, B=0, **ok), q=0) == 0
 
 
 def test_attn_fwd_argument_errors(fa):

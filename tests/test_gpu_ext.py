@@ -414,3 +414,87 @@ def test_workload_sparse_bwd_h16_n128k(fa):
                                         h_kv=h, keys=keys, rows=rows_k)
         assert_close(f"dK[kb{kb}]", dk[0, h, keys], np.stack([acc[j][0] for j in keys]), TOL_OUT)
         assert_close(f"dV[kb{kb}]", dv[0, h, keys], np.stack([acc[j][1] for j in keys]), TOL_OUT)
+
+
+# ----------------------------------------------------------------------------- fp8 (e4m3) inputs
+def dequant(x, n):
+    """fp64 values of an fp8 input: code x descale (exact)."""
+    return x[n].to(torch.float64) * x[n + "_descale"]
+
+
+def fp8_kw(x):
+    return dict(q_descale=x["q_descale"], k_descale=x["k_descale"], v_descale=x["v_descale"])
+
+
+FP8_CASES = [
+    # B, H, H_kv, N, d, causal, layout
+    (1, 2, 2, 300, 128, True, "bhnd"),
+    (2, 2, 1, 257, 64, False, "bnhd"),
+    (1, 4, 2, 64, 128, True, "bhnd"),
+    (1, 1, 1, 1, 128, False, "bhnd"),
+    (1, 2, 2, 640, 64, True, "bhnd"),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=lambda c: "b{}h{}kv{}n{}d{}{}{}".format(
+    c[0], c[1], c[2], c[3], c[4], "c" if c[5] else "", c[6]))
+def test_fp8_forward_small(fa, case):
+    B, H, Hkv, N, d, causal, layout = case
+    w = W.small(B, H, N, d, causal=causal, layout=layout, seed=30, H_kv=Hkv, dtype="fp8_e4m3")
+    x = W.make_inputs(w)
+    g = {n: x[n].to("cuda") for n in "qkv"}
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], causal=causal, scale=w.scale, **fp8_kw(x))
+    torch.cuda.synchronize()
+    assert o.dtype == torch.bfloat16
+    O, L = oracle.attention_forward(dequant(x, "q"), dequant(x, "k"), dequant(x, "v"), causal=causal,
+                                    scale=w.scale)
+    assert_close("O", o, O, TOL_OUT)
+    assert_close("LSE", lse, L, TOL_LSE)
+
+
+def test_fp8_sparse_and_packed(fa):
+    lens = (300, 700, 129)
+    w = W.small(H=2, d=128, causal=True, seed=31, seqlens=lens, dtype="fp8_e4m3")
+    x = W.make_inputs(w)
+    g = {n: x[n].to("cuda") for n in "qkv"}
+    cu = w.cu_seqlens()
+    off, idx, sp = lists_for((max(lens) + 127) // 128, 1, 3, True)
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], causal=True, scale=w.scale, cu_seqlens=cu, kv_offsets=off,
+                         kv_indices=idx, **fp8_kw(x))
+    torch.cuda.synchronize()
+    O, L = oracle.attention_forward_varlen(dequant(x, "q"), dequant(x, "k"), dequant(x, "v"), cu, causal=True,
+                                           scale=w.scale, sparse=sp)
+    assert_close("O", o, O, TOL_OUT)
+    assert_close("LSE", lse, L, TOL_LSE)
+
+
+def test_fp8_descales_scale_the_result(fa):
+    # the same codes with V's descale doubled give exactly twice the output (a power of two);
+    # doubling Q's descale and halving K's leaves the scores, so O and LSE are unchanged
+    w = W.small(1, 2, 500, 128, causal=True, seed=32, dtype="fp8_e4m3")
+    x = W.make_inputs(w)
+    g = {n: x[n].to("cuda") for n in "qkv"}
+    kw = fp8_kw(x)
+    o1, l1 = fa.attn_fwd(g["q"], g["k"], g["v"], causal=True, scale=w.scale, **kw)
+    o2, l2 = fa.attn_fwd(g["q"], g["k"], g["v"], causal=True, scale=w.scale,
+                         **{**kw, "v_descale": 2 * kw["v_descale"]})
+    o3, l3 = fa.attn_fwd(g["q"], g["k"], g["v"], causal=True, scale=w.scale,
+                         **{**kw, "q_descale": 2 * kw["q_descale"], "k_descale": kw["k_descale"] / 2})
+    torch.cuda.synchronize()
+    assert torch.equal(o2.float(), 2 * o1.float()) and torch.equal(l1, l2)
+    assert torch.equal(o3, o1) and torch.equal(l3, l1)
+
+
+def test_workload_fp8_h32_n32k(fa):
+    w = W.WORKLOADS["fp8_h32_n32k"]
+    x = W.make_inputs(w)
+    g = {n: x[n].to("cuda") for n in "qkv"}
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], causal=True, scale=w.scale, **fp8_kw(x))
+    torch.cuda.synchronize()
+    assert_finite("o", o)
+    rows = sample_rows(w.N, 256, np.random.default_rng(10), extra=16)[::4]
+    for h in (0, 17, 31):
+        sl = lambda n: dequant(x, n)[:, h:h + 1]
+        O, L = oracle.attention_forward(sl("q"), sl("k"), sl("v"), causal=True, scale=w.scale, rows=rows)
+        assert_close(f"O[h{h}]", o[0, h, rows], O[0, 0, rows], TOL_OUT)
+        assert_close(f"LSE[h{h}]", lse[0, h, rows], L[0, 0, rows], TOL_LSE)

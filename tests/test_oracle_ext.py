@@ -252,3 +252,35 @@ def test_sampled_key_gradients_match_autograd(sparse):
     for j in keys:
         np.testing.assert_allclose(got[j][0], k.grad[0, 1, j].numpy(), atol=1e-12)
         np.testing.assert_allclose(got[j][1], v.grad[0, 1, j].numpy(), atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- fp8 inputs
+def e4m3_by_definition(code: int) -> float:
+    """OCP 8-bit e4m3 (E4M3FN): sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0
+    holds the subnormals m/8 * 2^-6; S.1111.111 is NaN; there are no infinities."""
+    s, e, m = code >> 7, (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return math.nan
+    v = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+    return -v if s else v
+
+
+def test_fp8_e4m3_decode_matches_the_format_definition():
+    # the oracle sees fp8 inputs as code x descale in fp64; pin the code decoding used for it
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    got = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    want = np.array([e4m3_by_definition(c) for c in range(256)])
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2
+    np.testing.assert_array_equal(got[~nan], want[~nan])
+    assert want[~nan].max() == 448.0 and want[1] == 2.0 ** -9   # largest finite, smallest subnormal
+
+
+def test_fp8_dequantisation_is_exact_in_fp64():
+    # code (4 significant bits) x fp32 descale (24 bits) fits the 53-bit fp64 mantissa
+    import workloads as W
+    x = W.make_inputs(W.small(1, 2, 100, 64, seed=5, dtype="fp8_e4m3"))
+    q = x["q"].to(torch.float64).numpy()
+    deq = q * x["q_descale"]
+    assert np.array_equal(deq / x["q_descale"], q)
+    assert np.abs(q).max() <= 448.0

@@ -17,8 +17,11 @@ Five more cover the extensions: grouped K/V heads at the 32K shape and at the
 backward's shape (32 query heads over 8 K/V heads, the replication of the first page's
 GQA FAQ), a packed batch of variable-length sequences forward and backward (the first
 page's request batching; the pages give no length mix, so 16 lengths are drawn
-uniformly from [256, 8192] with a seeded numpy generator), and the backward of the
-128K block-sparse case (the third page's FAQ on training).
+uniformly from [256, 8192] with a seeded numpy generator), the backward of the
+128K block-sparse case (the third page's FAQ on training), and the 32K case with fp8
+(e4m3) inputs (the first page's FAQ on FP16 vs FP8): Q, K, V are drawn as for the bf16
+case, then each tensor gets the usual per-tensor scaling, descale = amax / 448, and is
+stored as e4m3 codes of x / descale (torch's round-to-nearest-even conversion).
 
 Drawing procedure (the pages name no RNG): a CPU ``torch.Generator`` seeded with the
 workload's seed draws Q, K, V and then dO, in that order, each as float32
@@ -51,6 +54,7 @@ class Workload:
     sparse: dict | None = field(default=None, hash=False)
     H_kv: int | None = None       # key/value heads (None: H)
     seqlens: tuple | None = None  # packed variable-length sequences (N is then the longest)
+    dtype: str = "bf16"           # "bf16" or "fp8_e4m3" (forward only)
 
     @property
     def hkv(self) -> int:
@@ -74,6 +78,8 @@ class Workload:
 
     def describe(self) -> str:
         heads = f"H={self.H}" + (f" H_kv={self.hkv}" if self.hkv != self.H else "")
+        if self.dtype != "bf16":
+            heads = f"{self.dtype} {heads}"
         if self.packed:
             s = (f"B={self.B} {heads} packed total={self.total} max_len={self.N} d={self.d} "
                  f"{'causal' if self.causal else 'non-causal'} sigma={self.sigma}")
@@ -114,7 +120,17 @@ WORKLOADS = {
                                    "packed", 1.0, 9, "bwd", seqlens=VARLEN_MIX),
     "sparse_bwd_h16_n128k": Workload("sparse_bwd_h16_n128k", 1, 16, 131072, 128, True, "bhnd", 1.0, 4,
                                      "sparse_bwd", SPARSE_128K),
+    "fp8_h32_n32k": Workload("fp8_h32_n32k", 1, 32, 32768, 128, True, "bhnd", 0.5, 10, "fwd", dtype="fp8_e4m3"),
 }
+
+FP8_MAX = 448.0   # largest finite e4m3 value
+
+
+def to_fp8(x: torch.Tensor):
+    """(e4m3 codes, descale) of an fp32 tensor with per-tensor scaling descale = amax / 448."""
+    amax = float(x.abs().max())
+    descale = float(torch.tensor(amax / FP8_MAX if amax > 0 else 1.0, dtype=torch.float32))
+    return (x / descale).to(torch.float8_e4m3fn), descale
 ORDER = list(WORKLOADS)
 
 
@@ -153,6 +169,17 @@ def make_inputs(w: Workload, with_grad: bool | None = None):
     else:
         qs = physical_shape(w)
         kvs = physical_shape(Workload(w.key, w.B, w.hkv, w.N, w.d, w.causal, w.layout))
+    if w.dtype == "fp8_e4m3":
+        raw = draw(qs, w.seed, w.sigma, 3, dtype=torch.float32) if qs == kvs else None
+        if raw is None:
+            g = torch.Generator(device="cpu").manual_seed(int(w.seed))
+            raw = [torch.randn(s, generator=g, dtype=torch.float32) * w.sigma for s in (qs, kvs, kvs)]
+        out = {}
+        for n, x in zip("qkv", raw):
+            code, ds = to_fp8(x)
+            out[n] = code if w.packed else to_logical(code, w.layout)
+            out[n + "_descale"] = ds
+        return out
     if qs == kvs:
         ts = draw(qs, w.seed, w.sigma, 4 if with_grad else 3)
     else:
@@ -170,10 +197,10 @@ def make_inputs(w: Workload, with_grad: bool | None = None):
 
 
 def small(B=1, H=1, N=256, d=64, causal=False, layout="bhnd", sigma=1.0, seed=0,
-          direction="fwd", sparse=None, H_kv=None, seqlens=None) -> Workload:
+          direction="fwd", sparse=None, H_kv=None, seqlens=None, dtype="bf16") -> Workload:
     """An ad-hoc small workload for tests (same drawing procedure)."""
     if seqlens is not None:
         seqlens = tuple(int(x) for x in seqlens)
         B, N, layout = len(seqlens), max(seqlens) if seqlens else 0, "packed"
     return Workload(f"small_b{B}h{H}n{N}d{d}", B, H, N, d, causal, layout, sigma, seed, direction, sparse,
-                    H_kv, seqlens)
+                    H_kv, seqlens, dtype)
