@@ -443,8 +443,11 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_kernel(Params p) {
         if (lp >= 0 && rows_valid) {
             const int t = lp >> 1;
             if ((lp & 1) == 0) {
+                // The matrix-product phase issues ahead of the other wave's softmax on its SIMD.
+                __builtin_amdgcn_s_setprio(1);
                 if (t >= 1 && t - 1 < Tw) pv<D, F8>(smem + ((t - 1) % kPPBufs) * C::BUF, w, i, hf);
                 if (t < Tw) scores<D, F8>(smem + (t % kPPBufs) * C::BUF, w, i, hf);
+                __builtin_amdgcn_s_setprio(0);
             } else if (t < Tw) {
                 const int kt = t * kBK;
                 const bool masked = (kt + kBK > N) || (CAUSAL && kt + kBK - 1 > qw0);
