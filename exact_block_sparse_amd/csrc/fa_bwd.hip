@@ -11,11 +11,11 @@
 // Q tile per block and would need a cross-block reduction for dK and dV):
 // 1. pre_kernel: D_i = dO_i . O_i, which equals sum_j P_ij dP_ij because O_i = sum_j P_ij V_j.
 //    Bandwidth-bound: it reads O and dO once.
-// 2. dkdv_kernel: a workgroup owns 128 keys (32 per wave, one key per lane column) and
-//    walks the query tiles that can see them. K and V of the wave's keys stay in
-//    registers as MFMA B operands; S = Q K^T and dP = dO V^T read Q and dO rows from LDS;
-//    dV^T += dO^T P and dK^T += Q^T dS read the transposed operands straight from the
-//    row-major tiles with ds_read_b64_tr_b16. dK^T, dV^T accumulate in fp32.
+// 2. dkdv16_kernel: a workgroup owns 128 keys (16 per wave, one key per lane column of
+//    16x16 products, 8 waves) and walks the query tiles that can see them. K and V of the
+//    wave's keys stay in registers as MFMA B operands; S = Q K^T and dP = dO V^T read Q and
+//    dO rows from LDS; dV^T += dO^T P and dK^T += Q^T dS read the transposed operands
+//    straight from the row-major tiles with ds_read_b64_tr_b16. dK^T, dV^T accumulate in fp32.
 // 3. dq_kernel: a workgroup owns 128 query rows, as in the forward, and walks the key
 //    tiles: S^T = K Q^T and dP^T = V dO^T with Q and dO in registers, then dQ^T += K^T dS^T
 //    with K^T read transposed from the row-major K tile.
@@ -48,18 +48,20 @@ struct BCfg {
 };
 
 // One 64-row tile of a [N, D] matrix (row stride sn elements) in registers: per thread CH
-// 16-byte chunks, loaded with a bounds-checked buffer load, stored to one or two LDS copies.
-template <int D>
+// 16-byte chunks (NT threads), loaded with a bounds-checked buffer load, stored to one or
+// two LDS copies.
+template <int D, int NT = kThreads>
 struct Tile {
     using C = BCfg<D>;
-    u32x4 r[C::CH];
-    uint32_t goff[C::CH];
-    int roff[C::CH], toff[C::CH];
+    static constexpr int CH = kStep * C::CR / NT;
+    u32x4 r[CH];
+    uint32_t goff[CH];
+    int roff[CH], toff[CH];
 
     __device__ void init(int tid, int64_t sn) {
 #pragma unroll
-        for (int j = 0; j < C::CH; ++j) {
-            const int id = tid + j * kThreads;
+        for (int j = 0; j < CH; ++j) {
+            const int id = tid + j * NT;
             const int row = id / C::CR, ch = id % C::CR;
             goff[j] = (uint32_t)(((int64_t)row * sn + 8 * ch) * 2);
             roff[j] = row * C::RS + 8 * ch;
@@ -69,11 +71,11 @@ struct Tile {
     __device__ void load(const uint16_t* base, int64_t sn, int r0, int N) {
         const auto rs = make_rsrc(base + (int64_t)r0 * sn, rows_bytes(r0, N, sn, D, kStep));
 #pragma unroll
-        for (int j = 0; j < C::CH; ++j) r[j] = buf_load16(rs, goff[j], 0);
+        for (int j = 0; j < CH; ++j) r[j] = buf_load16(rs, goff[j], 0);
     }
     __device__ void store(uint16_t* rowcopy, uint16_t* trcopy) const {
 #pragma unroll
-        for (int j = 0; j < C::CH; ++j) {
+        for (int j = 0; j < CH; ++j) {
             if (rowcopy) *reinterpret_cast<u32x4*>(rowcopy + roff[j]) = r[j];
             if (trcopy) *reinterpret_cast<u32x4*>(trcopy + toff[j]) = r[j];
         }
@@ -139,15 +141,30 @@ struct KVCfg {
     static_assert((STATS * 2) % 16 == 0 && (STAGE * 2) % 16 == 0, "16-byte alignment");
 };
 
+// dK, dV: a workgroup owns 128 keys, 16 per wave (v_mfma_f32_16x16x32_bf16), 8 waves. With
+// 32 keys per wave the dK, dV accumulators and the K, V operands alone take ~200 registers
+// and only one wave fits a SIMD; at 16 keys a wave needs ~190 in all, two waves share each
+// SIMD and hide each other's latencies (at twice the LDS reads per product).
+// Operand layout of the 16x16x32 product: lane l supplies row (A) / column (B) l % 16 and the
+// 8 k-values 8*(l/16) .. 8*(l/16)+7; accumulator element r of lane l is row 4*(l/16) + r,
+// column l % 16.
+constexpr int kThreads16 = 512;
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4v mfma16(bf16x8 a, bf16x8 b, f32x4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
+__global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
     using C = BCfg<D>;
     using L = KVCfg<D>;
-    constexpr int KSTEPS = C::KSTEPS, CB = C::CB;
+    constexpr int KS32 = D / 32;   // 32-wide k-steps over the head dimension
+    constexpr int CB16 = D / 16;   // 16-row blocks of dK^T, dV^T
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::STAGE];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, i = lane & 31;
+    const int wave = tid >> 6, lane = tid & 63, g = (lane >> 4) & 3, i = lane & 15;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int bhk = logical / p.nkb, kblk = logical % p.nkb;   // ascending: longest first under causal
     const int hk = bhk / p.B, b = bhk % p.B;   // head-major: an XCD's share spans every sequence
@@ -156,32 +173,37 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
     const int k0 = kblk * kKV_BK;
     if (k0 >= N) return;   // past the end of a shorter packed sequence (uniform per workgroup)
 
-    const int kw0 = k0 + 32 * wave;
+    const int kw0 = k0 + 16 * wave;
     const int key = kw0 + i;
 
-    // K and V rows of this lane's key as B operands (column = key, k-group = half).
-    bf16x8 kf[KSTEPS], vf[KSTEPS];
+    // K and V rows of this lane's key as B operands (column = key, k-group = g).
+    bf16x8 kf[KS32], vf[KS32];
     {
-        const uint16_t* kr = p.k + seq_off(sp, b, hk, p.ksb, p.ksh, p.ksn) + (int64_t)key * p.ksn + 8 * hf;
-        const uint16_t* vr = p.v + seq_off(sp, b, hk, p.vsb, p.vsh, p.vsn) + (int64_t)key * p.vsn + 8 * hf;
+        const uint16_t* kr = p.k + seq_off(sp, b, hk, p.ksb, p.ksh, p.ksn) + (int64_t)key * p.ksn + 8 * g;
+        const uint16_t* vr = p.v + seq_off(sp, b, hk, p.vsb, p.vsh, p.vsn) + (int64_t)key * p.vsn + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            kf[ks] = as_bf16x8(load16(kr + 16 * ks, key < N));
-            vf[ks] = as_bf16x8(load16(vr + 16 * ks, key < N));
+        for (int ks = 0; ks < KS32; ++ks) {
+            kf[ks] = as_bf16x8(load16(kr + 32 * ks, key < N));
+            vf[ks] = as_bf16x8(load16(vr + 32 * ks, key < N));
         }
     }
 
-    f32x16 dk[CB], dv[CB];
+    f32x4v dk[CB16], dv[CB16];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-        dk[cb] = f32x16{};
-        dv[cb] = f32x16{};
+    for (int cb = 0; cb < CB16; ++cb) {
+        dk[cb] = f32x4v{};
+        dv[cb] = f32x4v{};
     }
 
     // Steps: 64-row query tiles, for each of the G query heads that read this K/V head in
     // turn. Dense: the tiles from the first one that can see these keys (causal) or from 0 to
     // the end. Block-sparse: both halves of every query block the key-side list names for
-    // this key block; entries out of range (or, causal, above the diagonal) are skipped.
+    // this key block. Under causal masking only the steps of the diagonal block hold keys
+    // after queries: the first two of each query head (dense), or the two halves of the list's
+    // first entry when it is the diagonal block (lists ascend); they are taken first, so the
+    // others run without the element test. Out-of-range list entries (or, causal, entries
+    // above the diagonal) become an empty tile at row N: zero-filled loads, LSE = +inf, so
+    // their probabilities are exactly 0.
     const int nsteps = (N + kStep - 1) / kStep;
     const int t0 = CAUSAL ? k0 / kStep : 0;
     int64_t lo = 0, hi = 0;
@@ -192,30 +214,23 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
         lo = lo < 0 ? 0 : (lo > p.nnz ? p.nnz : lo);
         hi = hi < lo ? lo : (hi > p.nnz ? p.nnz : hi);
     }
-    const int per = sparse ? (int)(2 * (hi - lo)) : nsteps - t0;   // steps per query head
+    const int per = sparse ? (int)(2 * (hi - lo)) : nsteps - t0;
     const int n_all = per * p.G;
     const int nqb = (N + kKV_BK - 1) / kKV_BK;
-    // Under causal masking only the steps of the diagonal block (queries k0 .. k0+127) hold
-    // keys after queries: the first two steps of each query head (dense), or the two halves of
-    // the list's first entry when it is the diagonal block (block-sparse; lists ascend). They
-    // are taken first, for every query head, so that the rest run without the element test.
     const int m_per = !CAUSAL ? 0 : (sparse ? ((hi > lo && p.q_indices[lo] == kblk) ? 2 : 0) : min(2, per));
     const int n_mask = m_per * p.G;
     const int u_per = per - m_per;
-    // First query row of step s and its query head. Entries of the key-side list that are out
-    // of range (or, causal, above the diagonal) become an empty tile at row N: its loads are
-    // zero-filled and its rows get LSE = +inf, so its probabilities are exactly 0.
     auto step_row = [&](int s, int& hq) -> int {
-        int g, j;
+        int gq, j;
         if (s < n_mask) {
-            g = s / m_per;
-            j = s - g * m_per;
+            gq = s / m_per;
+            j = s - gq * m_per;
         } else {
             const int u = s - n_mask;
-            g = u / u_per;
-            j = m_per + (u - g * u_per);
+            gq = u / u_per;
+            j = m_per + (u - gq * u_per);
         }
-        hq = hk * p.G + g;
+        hq = hk * p.G + gq;
         if (!sparse) return (t0 + j) * kStep;
         const int qb = p.q_indices[lo + (j >> 1)];
         if (qb < 0 || qb >= nqb || (CAUSAL && qb < kblk)) return N;
@@ -224,7 +239,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
     };
     const float c = p.c;
 
-    Tile<D> tq, td;
+    Tile<D, kThreads16> tq, td;
     tq.init(tid, p.qsn);
     td.init(tid, p.dsn);
     float st_stat = 0.0f;
@@ -236,8 +251,6 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
         const int64_t so = seq_stat_off(sp, b, hq, p.H, p.N, p.total);
         if (tid < kStep) {
             const int row = r0 + tid;
-            // Rows past N get LSE = +inf, so their recomputed probabilities are exactly 0;
-            // so do rows that saw no key at all (LSE = -inf).
             float l = row < N ? p.lse[so + row] : __builtin_inff();
             if (l == -__builtin_inff()) l = __builtin_inff();
             st_stat = l * kLog2e;
@@ -252,128 +265,67 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
         if (tid < 2 * kStep) reinterpret_cast<float*>(s + L::STATS)[tid] = st_stat;
     };
 
-    // S = Q K^T and dP = dO V^T for the 32-query subtile qb of a stage (this wave's 32 keys).
-    auto sdp = [&](const uint16_t* s, int qb, f32x16& sacc, f32x16& pacc) {
-        sacc = f32x16{};
-        pacc = f32x16{};
-        const uint16_t* qr = s + L::QR + (32 * qb + i) * C::RS + 8 * hf;
-        const uint16_t* dr = s + L::DR + (32 * qb + i) * C::RS + 8 * hf;
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            sacc = mfma32(*reinterpret_cast<const bf16x8*>(qr + 16 * ks), kf[ks], sacc);
-            pacc = mfma32(*reinterpret_cast<const bf16x8*>(dr + 16 * ks), vf[ks], pacc);
-        }
-    };
-    // P = exp(S - LSE) and dS = P (dP - D) as bf16 operands. Element r of this lane is query
-    // qt0 + 32*qb + 8*(r/4) + 4*hf + r%4; with `mask`, keys after their query get P = 0.
-    auto probs = [&](bool mask, const uint16_t* s, int qb, int qt0, const f32x16& sacc, const f32x16& pacc,
-                     bf16x8 (&pb)[2], bf16x8 (&db)[2]) {
+    // Transposing-read lane base for a 16-wide column block: lane j of 16-lane group g addresses
+    // row 4*g + j/4, column 4*(j%4); it then receives rows 4g .. 4g+3 of column i.
+    const int tr_lane = (4 * g + (i >> 2)) * C::TS + 4 * (i & 3);
+
+    // One 32-query half (m) of a step: S, dP for its two 16-query tiles, probabilities, then
+    // dV^T += dO^T P and dK^T += Q^T dS. B element e of the P, dS operands is query
+    // 32m + 4g + e (e < 4) or 32m + 16 + 4g + e - 4, the order two transposing reads give A.
+    auto half = [&](bool mask, const uint16_t* s, int m, int qt0) {
         const float* sL = reinterpret_cast<const float*>(s + L::STATS);
         const float* sDel = sL + kStep;
-        float pv[16], dsv[16];
+        float pv[8], dsv[8];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + 32 * qb + 8 * g + 4 * hf);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(sDel + 32 * qb + 8 * g + 4 * hf);
+        for (int tt = 0; tt < 2; ++tt) {
+            const int q0 = 32 * m + 16 * tt;   // first query of the tile within the step
+            f32x4v sacc = {}, pacc = {};
+            const uint16_t* qr = s + L::QR + (q0 + i) * C::RS + 8 * g;
+            const uint16_t* dr = s + L::DR + (q0 + i) * C::RS + 8 * g;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * g + e;
-                float pe = fast_exp2(fmaf(sacc[r], c, -l4[e]));
-                if (mask && key > qt0 + 32 * qb + acc_row(r, hf)) pe = 0.0f;
-                pv[r] = pe;
-                dsv[r] = pe * (pacc[r] - d4[e]);
+            for (int ks = 0; ks < KS32; ++ks) {
+                sacc = mfma16(*reinterpret_cast<const bf16x8*>(qr + 32 * ks), kf[ks], sacc);
+                pacc = mfma16(*reinterpret_cast<const bf16x8*>(dr + 32 * ks), vf[ks], pacc);
+            }
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + q0 + 4 * g);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(sDel + q0 + 4 * g);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float pe = fast_exp2(fmaf(sacc[r], c, -l4[r]));
+                if (mask && key > qt0 + q0 + 4 * g + r) pe = 0.0f;
+                pv[4 * tt + r] = pe;
+                dsv[4 * tt + r] = pe * (pacc[r] - d4[r]);
             }
         }
+        const bf16x8 pb = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+        const bf16x8 db = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+        const uint16_t* qt = s + L::QT + tr_lane + 32 * m * C::TS;
+        const uint16_t* dt = s + L::DT + tr_lane + 32 * m * C::TS;
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            pb[st] = pack8(pv[8 * st], pv[8 * st + 1], pv[8 * st + 2], pv[8 * st + 3], pv[8 * st + 4],
-                           pv[8 * st + 5], pv[8 * st + 6], pv[8 * st + 7]);
-            db[st] = pack8(dsv[8 * st], dsv[8 * st + 1], dsv[8 * st + 2], dsv[8 * st + 3], dsv[8 * st + 4],
-                           dsv[8 * st + 5], dsv[8 * st + 6], dsv[8 * st + 7]);
+        for (int cb = 0; cb < CB16; ++cb) {
+            dv[cb] = mfma16(read_tr_operand16(dt + 16 * cb, C::TS), pb, dv[cb]);
+            dk[cb] = mfma16(read_tr_operand16(qt + 16 * cb, C::TS), db, dk[cb]);
         }
-    };
-    // dV^T += dO^T P and dK^T += Q^T dS over the subtile's 32 queries.
-    auto grads = [&](const uint16_t* s, int qb, const bf16x8 (&pb)[2], const bf16x8 (&db)[2]) {
-        const uint16_t* qt_base = tr_lane_base(s + L::QT, C::TS, lane);
-        const uint16_t* dt_base = tr_lane_base(s + L::DT, C::TS, lane);
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                const int off = (32 * qb + 16 * st) * C::TS + 32 * cb;
-                dv[cb] = mfma32(read_tr_operand(dt_base, off, C::TS), pb[st], dv[cb]);
-                dk[cb] = mfma32(read_tr_operand(qt_base, off, C::TS), db[st], dk[cb]);
-            }
     };
 
-    // Software pipeline over 32-query subtiles, so that the vector work of one subtile is
-    // issued next to independent matrix products: per step, the products S, dP of subtile 1
-    // run beside the probabilities of subtile 0, the gradient products of subtile 0 beside
-    // the probabilities of subtile 1; S, dP of the next step's subtile 0 follow the barrier
-    // that publishes its stage. Every wave takes every step (a fully masked subtile adds
-    // zeros), so the workgroup's waves stay in step between barriers.
     if (n_all > 0) {
         load_step(0);
         store_step(smem);
     }
-    // Settle every outstanding load (the K, V fragments included) so that no wait on them is
-    // left inside the loop; then start the loads of step 1.
     __builtin_amdgcn_s_waitcnt(0);
-    if (n_all > 1) load_step(1);
     __syncthreads();
-    f32x16 sA, dA, sB, dB;
-    int hq_unused;
-    int r_cur = N;
-    if (n_all > 0) {
-        r_cur = step_row(0, hq_unused);
-        sdp(smem, 0, sA, dA);
-    }
     int cur = 0;
     int t = 0;
     auto iterate = [&](bool mask) {
+        const bool has_next = t + 1 < n_all;
+        if (has_next) load_step(t + 1);
+        int hq_unused;
+        const int r0 = step_row(t, hq_unused);
         const uint16_t* s = smem + cur * L::STAGE;
-        uint16_t* s_next = smem + (cur ^ 1) * L::STAGE;
-        {
-            bf16x8 pa[2], da[2], pb[2], db[2];
-            sdp(s, 1, sB, dB);
-            probs(mask, s, 0, r_cur, sA, dA, pa, da);
-            grads(s, 0, pa, da);
-            probs(mask, s, 1, r_cur, sB, dB, pb, db);
-            grads(s, 1, pb, db);
-            // Issue order: one wave issues in order, so an MFMA run followed by a VALU run would
-            // not overlap, and an LDS read right before its MFMA exposes the read latency.
-            // Alternate each MFMA with about ten VALU operations of the other subtile's
-            // probabilities, and issue LDS reads several MFMAs ahead of their use:
-            // S, dP of subtile 1 beside subtile 0's probabilities; the gradient products of
-            // subtile 0 beside subtile 1's probabilities; then subtile 1's gradient products.
-            __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);          // LDS: stats, first rows
-#pragma unroll
-            for (int k = 0; k < 2 * KSTEPS; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
-                if (k < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);      // VALU
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-#pragma unroll
-            for (int k = 0; k < 4 * CB; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (k < 3 * CB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-            for (int k = 0; k < 4 * CB; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (k < 3 * CB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            }
-        }
-        if (t + 1 < n_all) store_step(s_next);
+        half(mask, s, 0, r0);
+        half(mask, s, 1, r0);
+        if (has_next) store_step(smem + (cur ^ 1) * L::STAGE);
         __syncthreads();
-        if (t + 2 < n_all) load_step(t + 2);
-        if (t + 1 < n_all) {
-            r_cur = step_row(t + 1, hq_unused);
-            sdp(s_next, 0, sA, dA);
-        }
         cur ^= 1;
     };
     for (; t < n_mask; ++t) iterate(true);
@@ -384,18 +336,16 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(KVParams p) {
         uint16_t* dvr = p.dv + seq_off(sp, b, hk, p.dvsb, p.dvsh, p.dvsn) + (int64_t)key * p.dvsn;
         const float sc = p.scale;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
+        for (int cb = 0; cb < CB16; ++cb) {
+            bf16x4 a, v;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                bf16x4 a, v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    a[e] = (__bf16)(dk[cb][4 * j + e] * sc);
-                    v[e] = (__bf16)(dv[cb][4 * j + e]);
-                }
-                *reinterpret_cast<bf16x4*>(dkr + 32 * cb + 8 * j + 4 * hf) = a;
-                *reinterpret_cast<bf16x4*>(dvr + 32 * cb + 8 * j + 4 * hf) = v;
+            for (int e = 0; e < 4; ++e) {
+                a[e] = (__bf16)(dk[cb][e] * sc);
+                v[e] = (__bf16)(dv[cb][e]);
             }
+            *reinterpret_cast<bf16x4*>(dkr + 16 * cb + 4 * g) = a;
+            *reinterpret_cast<bf16x4*>(dvr + 16 * cb + 4 * g) = v;
+        }
     }
 }
 
@@ -629,7 +579,7 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
         p.c = c;
         p.scale = a.scale;
         const int64_t grid = (int64_t)L.B * L.Hkv * p.nkb;
-        hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((dkdv16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads16), 0, stream, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -205,6 +205,17 @@ __device__ __forceinline__ bf16x8 read_tr_operand(const uint16_t* lane_base, int
     x[0] = lo[0]; x[1] = lo[1]; x[2] = hi[0]; x[3] = hi[1];
     return as_bf16x8(x);
 }
+// A operand of a 16x16x32 MFMA holding M^T (row = column of M, k = 8 rows of M), read from
+// a row-major bf16 tile (row stride `stride`) with two transposing reads; `p` is the lane's
+// address for rows 4*g .. 4*g+3 (g = lane / 16). Element e is row 4*g + e (e < 4) or
+// 16 + 4*g + e - 4 of M.
+__device__ __forceinline__ bf16x8 read_tr_operand16(const uint16_t* p, int stride) {
+    const u32x2 lo = lds_read_tr4(p);
+    const u32x2 hi = lds_read_tr4(p + 16 * stride);
+    u32x4 x;
+    x[0] = lo[0]; x[1] = lo[1]; x[2] = hi[0]; x[3] = hi[1];
+    return as_bf16x8(x);
+}
 __device__ __forceinline__ const uint16_t* tr_lane_base(const uint16_t* tile, int stride, int lane) {
     const int hf = lane >> 5, g = (lane >> 4) & 1, j = lane & 15;
     return tile + (4 * hf + (j >> 2)) * stride + 16 * g + 4 * (j & 3);
