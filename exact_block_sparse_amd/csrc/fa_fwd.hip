@@ -534,9 +534,15 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
         const uint16_t* buf = smem + cur * C::BUF;
         if (qw0 < N && (!CAUSAL || kt <= qw0 + 31)) {
             const bool masked = (kt + kBK > N) || (CAUSAL && kt + kBK - 1 > qw0);
+            // matrix products at raised priority: they issue ahead of the other workgroup's
+            // softmax on the same SIMD
+            __builtin_amdgcn_s_setprio(1);
             scores<D, F8>(buf, w, i, hf);
+            __builtin_amdgcn_s_setprio(0);
             softmax<D, F8, CAUSAL>(w, masked, kt, qrow, N, c, cpos, hf);
+            __builtin_amdgcn_s_setprio(1);
             pv<D, F8>(buf, w, i, hf);
+            __builtin_amdgcn_s_setprio(0);
         }
         if (has_next) st.store(smem + (cur ^ 1) * C::BUF);
         __syncthreads();
