@@ -50,7 +50,7 @@ struct BCfg {
 // One 64-row tile of a [N, D] matrix (row stride sn elements) in registers: per thread CH
 // 16-byte chunks (NT threads), loaded with a bounds-checked buffer load, stored to one or
 // two LDS copies.
-template <int D, int NT = kThreads>
+template <int D, int NT = kThreads, int TSTR = BCfg<D>::TS>
 struct Tile {
     using C = BCfg<D>;
     static constexpr int CH = kStep * C::CR / NT;
@@ -65,7 +65,7 @@ struct Tile {
             const int row = id / C::CR, ch = id % C::CR;
             goff[j] = (uint32_t)(((int64_t)row * sn + 8 * ch) * 2);
             roff[j] = row * C::RS + 8 * ch;
-            toff[j] = row * C::TS + 8 * ch;
+            toff[j] = row * TSTR + 8 * ch;
         }
     }
     __device__ void load(const uint16_t* base, int64_t sn, int r0, int N) {
@@ -134,9 +134,14 @@ struct KVParams {
 template <int D>
 struct KVCfg {
     using C = BCfg<D>;
+    // Transposed copies are read by 16x16-layout transposing reads: the two 16-lane groups
+    // served together read 8 different rows of 32 bytes, which a 288-byte row stride (72
+    // banks, 8 mod 64) keeps on disjoint banks (a 320-byte stride would pair rows r, r+4).
+    static constexpr int TS = D + 16;
+    static constexpr int TE = kStep * TS;
     // stage layout: Q rows | Q (transposed reads) | dO rows | dO (transposed reads) | lse2[64] | delta[64]
-    static constexpr int QR = 0, QT = C::RE, DR = C::RE + C::TE, DT = 2 * C::RE + C::TE;
-    static constexpr int STATS = 2 * C::RE + 2 * C::TE;
+    static constexpr int QR = 0, QT = C::RE, DR = C::RE + TE, DT = 2 * C::RE + TE;
+    static constexpr int STATS = 2 * C::RE + 2 * TE;
     static constexpr int STAGE = STATS + 2 * kStep * 2;   // in uint16 units
     static_assert((STATS * 2) % 16 == 0 && (STAGE * 2) % 16 == 0, "16-byte alignment");
 };
@@ -239,7 +244,7 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
     };
     const float c = p.c;
 
-    Tile<D, kThreads16> tq, td;
+    Tile<D, kThreads16, L::TS> tq, td;
     tq.init(tid, p.qsn);
     td.init(tid, p.dsn);
     float st_stat = 0.0f;
@@ -267,7 +272,7 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
 
     // Transposing-read lane base for a 16-wide column block: lane j of 16-lane group g addresses
     // row 4*g + j/4, column 4*(j%4); it then receives rows 4g .. 4g+3 of column i.
-    const int tr_lane = (4 * g + (i >> 2)) * C::TS + 4 * (i & 3);
+    const int tr_lane = (4 * g + (i >> 2)) * L::TS + 4 * (i & 3);
 
     // One 32-query half (m) of a step: S, dP for its two 16-query tiles, probabilities, then
     // dV^T += dO^T P and dK^T += Q^T dS. B element e of the P, dS operands is query
@@ -299,12 +304,12 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
         }
         const bf16x8 pb = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
         const bf16x8 db = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-        const uint16_t* qt = s + L::QT + tr_lane + 32 * m * C::TS;
-        const uint16_t* dt = s + L::DT + tr_lane + 32 * m * C::TS;
+        const uint16_t* qt = s + L::QT + tr_lane + 32 * m * L::TS;
+        const uint16_t* dt = s + L::DT + tr_lane + 32 * m * L::TS;
 #pragma unroll
         for (int cb = 0; cb < CB16; ++cb) {
-            dv[cb] = mfma16(read_tr_operand16(dt + 16 * cb, C::TS), pb, dv[cb]);
-            dk[cb] = mfma16(read_tr_operand16(qt + 16 * cb, C::TS), db, dk[cb]);
+            dv[cb] = mfma16(read_tr_operand16(dt + 16 * cb, L::TS), pb, dv[cb]);
+            dk[cb] = mfma16(read_tr_operand16(qt + 16 * cb, L::TS), db, dk[cb]);
         }
     };
 
