@@ -50,7 +50,7 @@ struct BCfg {
 // One 64-row tile of a [N, D] matrix (row stride sn elements) in registers: per thread CH
 // 16-byte chunks (NT threads), loaded with a bounds-checked buffer load, stored to one or
 // two LDS copies.
-template <int D, int NT = kThreads, int TSTR = BCfg<D>::TS>
+template <int D, int NT = kThreads, int RSTR = BCfg<D>::RS, int TSTR = BCfg<D>::TS>
 struct Tile {
     using C = BCfg<D>;
     static constexpr int CH = kStep * C::CR / NT;
@@ -64,7 +64,7 @@ struct Tile {
             const int id = tid + j * NT;
             const int row = id / C::CR, ch = id % C::CR;
             goff[j] = (uint32_t)(((int64_t)row * sn + 8 * ch) * 2);
-            roff[j] = row * C::RS + 8 * ch;
+            roff[j] = row * RSTR + 8 * ch;
             toff[j] = row * TSTR + 8 * ch;
         }
     }
@@ -134,14 +134,15 @@ struct KVParams {
 template <int D>
 struct KVCfg {
     using C = BCfg<D>;
-    // Transposed copies are read by 16x16-layout transposing reads: the two 16-lane groups
-    // served together read 8 different rows of 32 bytes, which a 288-byte row stride (72
-    // banks, 8 mod 64) keeps on disjoint banks (a 320-byte stride would pair rows r, r+4).
+    // One copy of each staged tile serves both of its read patterns, the 16-byte row reads of
+    // the 16x16 layout (4 lane groups x the same 16 rows) and the transposing reads (16 rows x
+    // 32 bytes, two 16-lane groups served together): both are free of bank conflicts at a
+    // 288-byte row stride (measured; 272 and 320 bytes each leave one of them 2-way).
     static constexpr int TS = D + 16;
     static constexpr int TE = kStep * TS;
-    // stage layout: Q rows | Q (transposed reads) | dO rows | dO (transposed reads) | lse2[64] | delta[64]
-    static constexpr int QR = 0, QT = C::RE, DR = C::RE + TE, DT = 2 * C::RE + TE;
-    static constexpr int STATS = 2 * C::RE + 2 * TE;
+    // stage layout: Q | dO | lse2[64] | delta[64]
+    static constexpr int QR = 0, DR = TE;
+    static constexpr int STATS = 2 * TE;
     static constexpr int STAGE = STATS + 2 * kStep * 2;   // in uint16 units
     static_assert((STATS * 2) % 16 == 0 && (STAGE * 2) % 16 == 0, "16-byte alignment");
 };
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
     };
     const float c = p.c;
 
-    Tile<D, kThreads16, L::TS> tq, td;
+    Tile<D, kThreads16, L::TS, L::TS> tq, td;
     tq.init(tid, p.qsn);
     td.init(tid, p.dsn);
     float st_stat = 0.0f;
@@ -265,8 +266,8 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
         }
     };
     auto store_step = [&](uint16_t* s) {
-        tq.store(s + L::QR, s + L::QT);
-        td.store(s + L::DR, s + L::DT);
+        tq.store(s + L::QR, nullptr);
+        td.store(s + L::DR, nullptr);
         if (tid < 2 * kStep) reinterpret_cast<float*>(s + L::STATS)[tid] = st_stat;
     };
 
@@ -277,39 +278,75 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
     // One 32-query half (m) of a step: S, dP for its two 16-query tiles, probabilities, then
     // dV^T += dO^T P and dK^T += Q^T dS. B element e of the P, dS operands is query
     // 32m + 4g + e (e < 4) or 32m + 16 + 4g + e - 4, the order two transposing reads give A.
-    auto half = [&](bool mask, const uint16_t* s, int m, int qt0) {
+    struct Acc { f32x4v s[2], p[2]; };
+    auto sdp = [&](const uint16_t* s, int m, Acc& a) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int q0 = 32 * m + 16 * tt;   // first query of the tile within the step
+            a.s[tt] = f32x4v{};
+            a.p[tt] = f32x4v{};
+            const uint16_t* qr = s + L::QR + (q0 + i) * L::TS + 8 * g;
+            const uint16_t* dr = s + L::DR + (q0 + i) * L::TS + 8 * g;
+#pragma unroll
+            for (int ks = 0; ks < KS32; ++ks) {
+                a.s[tt] = mfma16(*reinterpret_cast<const bf16x8*>(qr + 32 * ks), kf[ks], a.s[tt]);
+                a.p[tt] = mfma16(*reinterpret_cast<const bf16x8*>(dr + 32 * ks), vf[ks], a.p[tt]);
+            }
+        }
+    };
+    auto probs = [&](bool mask, const uint16_t* s, int m, int qt0, const Acc& a, bf16x8& pb, bf16x8& db) {
         const float* sL = reinterpret_cast<const float*>(s + L::STATS);
         const float* sDel = sL + kStep;
         float pv[8], dsv[8];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            const int q0 = 32 * m + 16 * tt;   // first query of the tile within the step
-            f32x4v sacc = {}, pacc = {};
-            const uint16_t* qr = s + L::QR + (q0 + i) * C::RS + 8 * g;
-            const uint16_t* dr = s + L::DR + (q0 + i) * C::RS + 8 * g;
-#pragma unroll
-            for (int ks = 0; ks < KS32; ++ks) {
-                sacc = mfma16(*reinterpret_cast<const bf16x8*>(qr + 32 * ks), kf[ks], sacc);
-                pacc = mfma16(*reinterpret_cast<const bf16x8*>(dr + 32 * ks), vf[ks], pacc);
-            }
+            const int q0 = 32 * m + 16 * tt;
             const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + q0 + 4 * g);
             const f32x4 d4 = *reinterpret_cast<const f32x4*>(sDel + q0 + 4 * g);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float pe = fast_exp2(fmaf(sacc[r], c, -l4[r]));
+                float pe = fast_exp2(fmaf(a.s[tt][r], c, -l4[r]));
                 if (mask && key > qt0 + q0 + 4 * g + r) pe = 0.0f;
                 pv[4 * tt + r] = pe;
-                dsv[4 * tt + r] = pe * (pacc[r] - d4[r]);
+                dsv[4 * tt + r] = pe * (a.p[tt][r] - d4[r]);
             }
         }
-        const bf16x8 pb = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-        const bf16x8 db = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-        const uint16_t* qt = s + L::QT + tr_lane + 32 * m * L::TS;
-        const uint16_t* dt = s + L::DT + tr_lane + 32 * m * L::TS;
+        pb = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+        db = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+    };
+    auto grads = [&](const uint16_t* s, int m, const bf16x8& pb, const bf16x8& db) {
+        const uint16_t* qt = s + L::QR + tr_lane + 32 * m * L::TS;
+        const uint16_t* dt = s + L::DR + tr_lane + 32 * m * L::TS;
 #pragma unroll
         for (int cb = 0; cb < CB16; ++cb) {
             dv[cb] = mfma16(read_tr_operand16(dt + 16 * cb, L::TS), pb, dv[cb]);
             dk[cb] = mfma16(read_tr_operand16(qt + 16 * cb, L::TS), db, dk[cb]);
+        }
+    };
+    // A step as a pipeline inside the wave, so that each half's exponentials sit beside
+    // independent matrix products: S, dP of half 0; S, dP of half 1 beside half 0's
+    // probabilities; the gradient products of half 0 beside half 1's probabilities; then
+    // half 1's gradient products. Scheduling-group hints alternate the two streams.
+    auto step = [&](bool mask, const uint16_t* s, int qt0) {
+        Acc a0, a1;
+        bf16x8 pb0, db0, pb1, db1;
+        sdp(s, 0, a0);
+        sdp(s, 1, a1);
+        probs(mask, s, 0, qt0, a0, pb0, db0);
+        grads(s, 0, pb0, db0);
+        probs(mask, s, 1, qt0, a1, pb1, db1);
+        grads(s, 1, pb1, db1);
+#pragma unroll
+        for (int k = 0; k < 4 * KS32; ++k) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // S, dP half 0
+#pragma unroll
+        for (int k = 0; k < 4 * KS32; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // S, dP half 1
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // probabilities half 0
+        }
+#pragma unroll
+        for (int k = 0; k < 2 * CB16; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // gradients half 0
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // probabilities half 1
         }
     };
 
@@ -327,8 +364,7 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
         int hq_unused;
         const int r0 = step_row(t, hq_unused);
         const uint16_t* s = smem + cur * L::STAGE;
-        half(mask, s, 0, r0);
-        half(mask, s, 1, r0);
+        step(mask, s, r0);
         if (has_next) store_step(smem + (cur ^ 1) * L::STAGE);
         __syncthreads();
         cur ^= 1;
