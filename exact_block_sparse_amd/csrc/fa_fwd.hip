@@ -207,6 +207,16 @@ __device__ __forceinline__ void scores(const uint16_t* buf, Rows<D, F8>& w, int 
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
                 w.s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kr + 32 * kb * C::KS + 16 * ks), w.qf.v[ks], w.s[kb]);
+        // Issue the K reads several products ahead of their use, so that the LDS latency is
+        // covered by earlier products rather than waited for before each one.
+        constexpr int N = 2 * C::KSTEPS, AHEAD = 6;
+        __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+        for (int k = 0; k < N - AHEAD; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
     } else {
         // lane (key i, half hf) reads the 32 bytes 32*hf + 64*ks .. of its K row
         const uint8_t* kr = reinterpret_cast<const uint8_t*>(buf) + i * C::KROWB + 32 * hf;
