@@ -209,7 +209,7 @@ __device__ __forceinline__ void scores(const uint16_t* buf, Rows<D, F8>& w, int 
                 w.s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kr + 32 * kb * C::KS + 16 * ks), w.qf.v[ks], w.s[kb]);
         // Issue the K reads several products ahead of their use, so that the LDS latency is
         // covered by earlier products rather than waited for before each one.
-        constexpr int N = 2 * C::KSTEPS, AHEAD = 6;
+        constexpr int N = 2 * C::KSTEPS, AHEAD = N < 6 ? N : 6;
         __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
 #pragma unroll
         for (int k = 0; k < N - AHEAD; ++k) {
