@@ -171,7 +171,9 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, g = (lane >> 4) & 3, i = lane & 15;
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    // Block-sparse: plain order, so that all XCDs work on the same head at once and its
+    // Q/dO stay in the cache they share (key-side lists reach across the whole head).
+    const int logical = p.q_offsets ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
     const int bhk = logical / p.nkb, kblk = logical % p.nkb;   // ascending: longest first under causal
     const int hk = bhk / p.B, b = bhk % p.B;   // head-major: an XCD's share spans every sequence
     const SeqSpan sp = seq_span(p.cu, p.total, b, p.N);
@@ -215,15 +217,15 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
     int64_t lo = 0, hi = 0;
     const bool sparse = p.q_offsets != nullptr;
     if (sparse) {
-        lo = p.q_offsets[kblk];
-        hi = p.q_offsets[kblk + 1];
+        lo = load_uniform(p.q_offsets, kblk);
+        hi = load_uniform(p.q_offsets, kblk + 1);
         lo = lo < 0 ? 0 : (lo > p.nnz ? p.nnz : lo);
         hi = hi < lo ? lo : (hi > p.nnz ? p.nnz : hi);
     }
     const int per = sparse ? (int)(2 * (hi - lo)) : nsteps - t0;
     const int n_all = per * p.G;
     const int nqb = (N + kKV_BK - 1) / kKV_BK;
-    const int m_per = !CAUSAL ? 0 : (sparse ? ((hi > lo && p.q_indices[lo] == kblk) ? 2 : 0) : min(2, per));
+    const int m_per = !CAUSAL ? 0 : (sparse ? ((hi > lo && load_uniform(p.q_indices, lo) == kblk) ? 2 : 0) : min(2, per));
     const int n_mask = m_per * p.G;
     const int u_per = per - m_per;
     auto step_row = [&](int s, int& hq) -> int {
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
         }
         hq = hk * p.G + gq;
         if (!sparse) return (t0 + j) * kStep;
-        const int qb = p.q_indices[lo + (j >> 1)];
+        const int qb = load_uniform(p.q_indices, lo + (j >> 1));
         if (qb < 0 || qb >= nqb || (CAUSAL && qb < kblk)) return N;
         const int r0 = qb * kKV_BK + (j & 1) * kStep;
         return r0 < N ? r0 : N;
@@ -429,7 +431,9 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(QParams p) {
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, i = lane & 31;
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    // Block-sparse: plain order, so that all XCDs work on the same head at once and its K/V
+    // stay in the cache they share (strided lists reach back over the whole head).
+    const int logical = p.kv_offsets ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
     const int bh = logical / p.nqb;
     int qb = logical % p.nqb;
     if (CAUSAL) qb = p.nqb - 1 - qb;
@@ -477,8 +481,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(QParams p) {
     const bool sparse = p.kv_offsets != nullptr;
     int64_t lo = 0;
     if (sparse) {
-        int64_t hi = p.kv_offsets[qb + 1];
-        lo = p.kv_offsets[qb];
+        int64_t hi = load_uniform(p.kv_offsets, qb + 1);
+        lo = load_uniform(p.kv_offsets, qb);
         lo = lo < 0 ? 0 : (lo > p.nnz ? p.nnz : lo);
         hi = hi < lo ? lo : (hi > p.nnz ? p.nnz : hi);
         nsteps = (int)(2 * (hi - lo));
@@ -486,7 +490,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(QParams p) {
     const int nkb = (N + kQ_BQ - 1) / kQ_BQ;
     auto step_key = [&](int t) -> int {   // first key of step t, or -1 to skip it
         if (!sparse) return t * kStep;
-        const int kb = p.kv_indices[lo + (t >> 1)];
+        const int kb = load_uniform(p.kv_indices, lo + (t >> 1));
         if (kb < 0 || kb >= nkb || (CAUSAL && kb > qb)) return -1;
         const int kt0 = kb * kQ_BQ + (t & 1) * kStep;
         return (kt0 < N && (!CAUSAL || kt0 <= qlast)) ? kt0 : -1;

@@ -48,6 +48,13 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Element of a table that stays unchanged while the kernel runs (the block lists), read
+// with a wave-uniform index. Through the constant address space the read can be a scalar
+// load, which does not make the wave wait for its vector loads still in flight.
+__device__ __forceinline__ int32_t load_uniform(const int32_t* table, int64_t idx) {
+    return ((const __attribute__((address_space(4))) int32_t*)table)[idx];
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }

@@ -482,10 +482,13 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, i = lane & 31;
 
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = logical / p.nqb;
-    const int qblk = p.nqb - 1 - logical % p.nqb;   // longest lists first
-    const int hh = bh / p.B, b = bh % p.B;   // head-major: an XCD's share spans every sequence
+    // Plain order, longest lists first. Consecutive ids go to the 8 XCDs in turn, so all of
+    // them work on the same head at once: a strided list reaches back over the whole head,
+    // and the head's K/V then stays in the cache the XCDs share (giving each XCD its own
+    // heads, as the dense kernel does, overflows it).
+    const int bh = blockIdx.x / p.nqb;
+    const int qblk = p.nqb - 1 - blockIdx.x % p.nqb;
+    const int hh = bh / p.B, b = bh % p.B;   // head-major: the sequences of a head are adjacent
     const SeqSpan sp = seq_span(p.cu, p.total, b, p.N);
     const int N = sp.len;
     const int q0 = qblk * kSparseBlock;
@@ -505,13 +508,13 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
     // Step t covers half (t & 1) of the listed key block kv_indices[t >> 1]. Offsets are
     // clamped to [0, nnz]; out-of-range and (causal) above-diagonal entries are skipped.
     const int nkb = (N + kSparseBlock - 1) / kSparseBlock;
-    int64_t lo = p.kv_offsets[qblk], hi = p.kv_offsets[qblk + 1];
+    int64_t lo = load_uniform(p.kv_offsets, qblk), hi = load_uniform(p.kv_offsets, qblk + 1);
     lo = lo < 0 ? 0 : (lo > p.nnz ? p.nnz : lo);
     hi = hi < lo ? lo : (hi > p.nnz ? p.nnz : hi);
     int t = (int)(2 * lo);
     const int t_end = (int)(2 * hi);
     auto step_key = [&](int tt) -> int {   // first key of step tt, or -1 to skip it
-        const int kblk = p.kv_indices[tt >> 1];
+        const int kblk = load_uniform(p.kv_indices, tt >> 1);
         if (kblk < 0 || kblk >= nkb || (CAUSAL && kblk > qblk)) return -1;
         const int kt0 = kblk * kSparseBlock + (tt & 1) * kBK;
         if (kt0 >= N || (CAUSAL && kt0 > qlast)) return -1;
