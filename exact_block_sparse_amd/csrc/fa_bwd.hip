@@ -50,11 +50,11 @@ struct BCfg {
 // One 64-row tile of a [N, D] matrix (row stride sn elements) in registers: per thread CH
 // 16-byte chunks (NT threads), loaded with a bounds-checked buffer load, stored to one or
 // two LDS copies.
-template <int D, int NT = kThreads, int RSTR = BCfg<D>::RS, int TSTR = BCfg<D>::TS>
+template <int D, int NT = kThreads, int RSTR = BCfg<D>::RS, int TSTR = BCfg<D>::TS, int SETS = 1>
 struct Tile {
     using C = BCfg<D>;
     static constexpr int CH = kStep * C::CR / NT;
-    u32x4 r[CH];
+    u32x4 r[SETS][CH];   // SETS register sets: loads for different steps in flight at once
     uint32_t goff[CH];
     int roff[CH], toff[CH];
 
@@ -68,16 +68,18 @@ struct Tile {
             toff[j] = row * TSTR + 8 * ch;
         }
     }
+    template <int S = 0>
     __device__ void load(const uint16_t* base, int64_t sn, int r0, int N) {
         const auto rs = make_rsrc(base + (int64_t)r0 * sn, rows_bytes(r0, N, sn, D, kStep));
 #pragma unroll
-        for (int j = 0; j < CH; ++j) r[j] = buf_load16(rs, goff[j], 0);
+        for (int j = 0; j < CH; ++j) r[S][j] = buf_load16(rs, goff[j], 0);
     }
+    template <int S = 0>
     __device__ void store(uint16_t* rowcopy, uint16_t* trcopy) const {
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
-            if (rowcopy) *reinterpret_cast<u32x4*>(rowcopy + roff[j]) = r[j];
-            if (trcopy) *reinterpret_cast<u32x4*>(trcopy + toff[j]) = r[j];
+            if (rowcopy) *reinterpret_cast<u32x4*>(rowcopy + roff[j]) = r[S][j];
+            if (trcopy) *reinterpret_cast<u32x4*>(trcopy + toff[j]) = r[S][j];
         }
     }
 };
@@ -171,6 +173,7 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, g = (lane >> 4) & 3, i = lane & 15;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     // Block-sparse: plain order, so that all XCDs work on the same head at once and its
     // Q/dO stay in the cache they share (key-side lists reach across the whole head).
     const int logical = p.q_offsets ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
@@ -228,7 +231,11 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
     const int m_per = !CAUSAL ? 0 : (sparse ? ((hi > lo && load_uniform(p.q_indices, lo) == kblk) ? 2 : 0) : min(2, per));
     const int n_mask = m_per * p.G;
     const int u_per = per - m_per;
-    auto step_row = [&](int s, int& hq) -> int {
+    auto step_row = [&](int s, int& hq) -> int {   // first row of step s; N past the last step
+        if (s >= n_all) {
+            hq = hk * p.G;
+            return N;
+        }
         int gq, j;
         if (s < n_mask) {
             gq = s / m_per;
@@ -247,30 +254,39 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
     };
     const float c = p.c;
 
-    Tile<D, kThreads16, L::TS, L::TS> tq, td;
+    // Staging in two register sets: the loads of step t + 2 are issued at the start of step t
+    // (into the set step t's data has just left) and stored to LDS at the end of step t + 1.
+    Tile<D, kThreads16, L::TS, L::TS, 2> tq, td;
     tq.init(tid, p.qsn);
     td.init(tid, p.dsn);
-    float st_stat = 0.0f;
-    auto load_step = [&](int s) {
+    float st_stat[2] = {0.0f, 0.0f};
+    auto load_step = [&](auto set, int s) {   // steps past the last one load nothing (zeros)
+        constexpr int S = decltype(set)::value;
         int hq;
         const int r0 = step_row(s, hq);
-        tq.load(p.q + seq_off(sp, b, hq, p.qsb, p.qsh, p.qsn), p.qsn, r0, N);
-        td.load(p.dout + seq_off(sp, b, hq, p.dsb, p.dsh, p.dsn), p.dsn, r0, N);
+        tq.template load<S>(p.q + seq_off(sp, b, hq, p.qsb, p.qsh, p.qsn), p.qsn, r0, N);
+        td.template load<S>(p.dout + seq_off(sp, b, hq, p.dsb, p.dsh, p.dsn), p.dsn, r0, N);
         const int64_t so = seq_stat_off(sp, b, hq, p.H, p.N, p.total);
-        if (tid < kStep) {
-            const int row = r0 + tid;
-            float l = row < N ? p.lse[so + row] : __builtin_inff();
-            if (l == -__builtin_inff()) l = __builtin_inff();
-            st_stat = l * kLog2e;
-        } else if (tid < 2 * kStep) {
-            const int row = r0 + tid - kStep;
-            st_stat = row < N ? p.delta[so + row] : 0.0f;
-        }
+        // Raw LSE (wave 0) and D (wave 1), one row per lane; the LSE is converted when stored,
+        // so that nothing waits for these loads before then. The branch is on a wave-uniform
+        // value, so each wave loads through its own pointer.
+        static_assert(kStep == 64, "one stats row per lane of waves 0 and 1");
+        const int row = r0 + lane;
+        if (wave_u == 0) st_stat[S] = row < N ? p.lse[so + row] : __builtin_inff();
+        else if (wave_u == 1) st_stat[S] = row < N ? p.delta[so + row] : 0.0f;
     };
-    auto store_step = [&](uint16_t* s) {
-        tq.store(s + L::QR, nullptr);
-        td.store(s + L::DR, nullptr);
-        if (tid < 2 * kStep) reinterpret_cast<float*>(s + L::STATS)[tid] = st_stat;
+    auto store_step = [&](auto set, uint16_t* s) {
+        constexpr int S = decltype(set)::value;
+        tq.template store<S>(s + L::QR, nullptr);
+        td.template store<S>(s + L::DR, nullptr);
+        if (tid < kStep) {
+            // exp2 domain; an LSE of -inf (a row with no allowed key) becomes +inf so that its
+            // probabilities are exactly 0
+            const float l = st_stat[S];
+            reinterpret_cast<float*>(s + L::STATS)[tid] = (l == -__builtin_inff() ? __builtin_inff() : l) * kLog2e;
+        } else if (tid < 2 * kStep) {
+            reinterpret_cast<float*>(s + L::STATS)[tid] = st_stat[S];
+        }
     };
 
     // Transposing-read lane base for a 16-wide column block: lane j of 16-lane group g addresses
@@ -352,27 +368,41 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
         }
     };
 
+    using Set0 = std::integral_constant<int, 0>;
+    using Set1 = std::integral_constant<int, 1>;
     if (n_all > 0) {
-        load_step(0);
-        store_step(smem);
+        load_step(Set0{}, 0);
+        store_step(Set0{}, smem);
     }
+    // Settle every outstanding load (the K, V rows included) so that no wait on them is left
+    // inside the loop; then start the loads of step 1.
     __builtin_amdgcn_s_waitcnt(0);
+    load_step(Set1{}, 1);
     __syncthreads();
-    int cur = 0;
+    // Step t runs from LDS stage t % 2 with register set t % 2; the loops take steps in pairs
+    // so that both are fixed at compile time. The masked steps are an even number except when
+    // a key block sees a single step, and then every step is masked.
     int t = 0;
-    auto iterate = [&](bool mask) {
-        const bool has_next = t + 1 < n_all;
-        if (has_next) load_step(t + 1);
+    auto iterate = [&](auto set, bool mask) {
+        constexpr int S = decltype(set)::value;
+        load_step(set, t + 2);
         int hq_unused;
         const int r0 = step_row(t, hq_unused);
-        const uint16_t* s = smem + cur * L::STAGE;
-        step(mask, s, r0);
-        if (has_next) store_step(smem + (cur ^ 1) * L::STAGE);
+        step(mask, smem + S * L::STAGE, r0);
+        store_step(std::integral_constant<int, 1 - S>{}, smem + (1 - S) * L::STAGE);   // step t + 1
         __syncthreads();
-        cur ^= 1;
+        ++t;
     };
-    for (; t < n_mask; ++t) iterate(true);
-    for (; t < n_all; ++t) iterate(false);
+    while (t + 1 < n_mask) {
+        iterate(Set0{}, true);
+        iterate(Set1{}, true);
+    }
+    if (t < n_mask) iterate(Set0{}, true);
+    while (t + 1 < n_all) {
+        iterate(Set0{}, false);
+        iterate(Set1{}, false);
+    }
+    if (t < n_all) iterate(Set0{}, false);
 
     if (key < N) {
         uint16_t* dkr = p.dk + seq_off(sp, b, hk, p.dksb, p.dksh, p.dksn) + (int64_t)key * p.dksn;
