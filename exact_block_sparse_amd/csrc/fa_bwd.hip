@@ -354,17 +354,26 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
         grads(s, 0, pb0, db0);
         probs(mask, s, 1, qt0, a1, pb1, db1);
         grads(s, 1, pb1, db1);
+        // LDS reads run AHEAD ahead of the products that use them: one 16-byte read per S/dP
+        // product, two transposing reads per gradient product.
+        constexpr int AHEAD = 6;
+        __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
 #pragma unroll
-        for (int k = 0; k < 4 * KS32; ++k) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // S, dP half 0
+        for (int k = 0; k < 4 * KS32; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // S, dP half 0
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
 #pragma unroll
         for (int k = 0; k < 4 * KS32; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // S, dP half 1
             __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // probabilities half 0
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
 #pragma unroll
         for (int k = 0; k < 2 * CB16; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // gradients half 0
             __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // probabilities half 1
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
     };
 
