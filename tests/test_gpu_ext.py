@@ -88,6 +88,9 @@ GQA_BWD = [
     (1, 4, 2, 200, 128, True, 1.0),
     (2, 6, 3, 130, 64, False, 1.0),
     (1, 4, 1, 257, 128, True, 0.5),
+    # three query heads per K/V head, causal, N = 130: the last key block sees one query
+    # step per head (an odd number of masked steps), the first an odd number of unmasked ones
+    (1, 6, 2, 130, 128, True, 0.5),
 ]
 
 
