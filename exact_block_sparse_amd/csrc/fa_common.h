@@ -28,11 +28,6 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // Row of the 32x32 accumulator held in element r by a lane of half `hf` (= lane / 32).
 __device__ __forceinline__ int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
 
-// Swap bits 2 and 3 of a row index in [0, 32). Loading A-operand row i from key
-// swz(i) makes the accumulator row order, read back as a B operand, name 8 consecutive
-// keys per lane: B element e of k-step s in half hf is key 16*s + 8*hf + e.
-__device__ __forceinline__ int swz(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
-
 // Combine a value with the one held by the lane 32 positions away (the other half of the
 // wave), with a symmetric op: the two halves hold complementary keys of the same query.
 __device__ __forceinline__ float pair_max(float x) {
@@ -83,23 +78,6 @@ __device__ __forceinline__ int xcd_remap(int w, int G) {
     const int per = G / X, rem = G % X;
     return x * per + (x < rem ? x : rem) + slot;
 }
-
-// Transpose four 16-byte rows (4 keys x 8 head-dim values, bf16) into eight 8-byte
-// columns (8 head-dim values x 4 keys) written at dst + c*row_stride, c = 0..7.
-__device__ __forceinline__ void store_transposed_4x8(uint16_t* dst, int row_stride, const u32x4& r0,
-                                                     const u32x4& r1, const u32x4& r2, const u32x4& r3) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        u32x2 even, odd;
-        even[0] = (r0[w] & 0xffffu) | (r1[w] << 16);
-        even[1] = (r2[w] & 0xffffu) | (r3[w] << 16);
-        odd[0] = (r0[w] >> 16) | (r1[w] & 0xffff0000u);
-        odd[1] = (r2[w] >> 16) | (r3[w] & 0xffff0000u);
-        *reinterpret_cast<u32x2*>(dst + (2 * w) * row_stride) = even;
-        *reinterpret_cast<u32x2*>(dst + (2 * w + 1) * row_stride) = odd;
-    }
-}
-
 
 // Raw buffer resource over [base, base + bytes): loads at byte offsets >= bytes return 0
 // without touching memory (the hardware range check), which gives zero-filled tails.

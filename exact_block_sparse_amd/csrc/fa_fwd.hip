@@ -29,10 +29,11 @@
 // * dense kernel ("ping-pong"): 8 waves and 256 query rows per workgroup, in two groups of
 //   four that alternate phase by phase: while one group runs its matrix products (P.V of
 //   the previous tile, then S of the current one) the other runs its softmax on the vector
-//   ALU. Each SIMD holds one wave of each group, so the MFMA pipe and the VALU work at the
-//   same time. Tiles cycle through three LDS buffers so loads run two tiles ahead;
+//   ALU. Each SIMD holds one wave of each group, so one wave's products and the other's
+//   softmax are issued side by side (they overlap only in part: each slows the other).
+//   Tiles cycle through three LDS buffers so loads run two tiles ahead;
 // * sparse kernel: 4 waves and one 128-row block per workgroup (the list granularity),
-//   two workgroups per CU, each step in one go;
+//   two workgroups per CU, each step in one go, workgroups in plain order;
 // * the LSE is written in natural log, O as bf16.
 #include "fa_common.h"
 #include "fa_internal.h"
