@@ -111,6 +111,7 @@ SPARSE_CASES = [
     (2, 1, 128 * 9, 64, True, 1, 4, "fixed"),
     (1, 1, 128 * 7 + 1, 128, False, 1, 3, "strided"),
     (1, 2, 128 * 6, 128, True, 10, 0, "strided"),     # window covers everything: causal dense
+    (2, 3, 128 * 5 + 17, 128, True, 1, 2, "strided"),  # several sequences and heads, ragged tail
 ]
 
 
