@@ -166,6 +166,28 @@ def test_sparse_device_lists_out_of_range_entries_are_skipped(fa):
     assert_close("LSE", lse, L_ref, TOL_LSE)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_scores_far_above_the_first_tile(fa, causal):
+    # Keys after the first 64 are scaled up 30x, so later scores exceed the first tile's
+    # maximum by far more than 64 in the exp2 domain: the running max must move on a tile
+    # whose probabilities would otherwise overflow (the rare path of the online softmax).
+    x = small_inputs(1, 2, 300, 128, seed=41)
+    k = x["k"].float()
+    k[:, :, 64:] *= 30.0
+    k = k.to(torch.bfloat16)
+    sc = scale_for(128)
+    o, lse = fa.fwd(to_dev(x["q"]), to_dev(k), to_dev(x["v"]), causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_forward(x["q"], k, x["v"], causal=causal, scale=sc)
+    # the case really crosses the threshold: some row's later scores exceed its first-tile
+    # maximum by more than 64 in the exp2 domain
+    S = sc * np.log2(np.e) * np.einsum("bhid,bhjd->bhij", f64(x["q"]), f64(k))
+    gap = S[..., 64:128, 64:].max(axis=-1) - S[..., 64:128, :64].max(axis=-1)
+    assert gap.max() > 64
+    assert_close("O", o, O, TOL_OUT)
+    assert_close("LSE", lse, L, TOL_LSE)
+
+
 # ----------------------------------------------------------------------------- backward, small
 BWD_CASES = [
     (1, 1, 64, 64, False, "bhnd"),
