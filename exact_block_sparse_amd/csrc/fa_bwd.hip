@@ -151,8 +151,9 @@ struct KVCfg {
 
 // dK, dV: a workgroup owns 128 keys, 16 per wave (v_mfma_f32_16x16x32_bf16), 8 waves. With
 // 32 keys per wave the dK, dV accumulators and the K, V operands alone take ~200 registers
-// and only one wave fits a SIMD; at 16 keys a wave needs ~190 in all, two waves share each
-// SIMD and hide each other's latencies (at twice the LDS reads per product).
+// and only one wave fits a SIMD; at 16 keys a wave needs ~220 in all (two staging sets
+// included), two waves share each SIMD and hide each other's latencies (at twice the LDS
+// reads per product).
 // Operand layout of the 16x16x32 product: lane l supplies row (A) / column (B) l % 16 and the
 // 8 k-values 8*(l/16) .. 8*(l/16)+7; accumulator element r of lane l is row 4*(l/16) + r,
 // column l % 16.
