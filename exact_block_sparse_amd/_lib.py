@@ -43,7 +43,7 @@ class FaError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m exact_block_sparse_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python exact_block_sparse_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     pi32 = ctypes.POINTER(ctypes.c_int32)

@@ -1,6 +1,7 @@
 """Build libfa.so in place: hipcc for gfx950, one object per source, then one link.
 
-Usage: python -m exact_block_sparse_amd.build  (or call build()).
+Usage: python exact_block_sparse_amd/build.py  (or call build()); run as a file, since importing
+the package needs the library it builds.
 The library lands next to this file; build products go to _build/ at the repo root.
 """
 from __future__ import annotations
