@@ -335,6 +335,17 @@ __device__ __forceinline__ void pv(const uint16_t* buf, Rows<D, F8>& w, int i, i
 #pragma unroll
             for (int st = 0; st < 2; ++st) w.o[cb] = mfma32(a[kb][st], w.pb[kb][st], w.o[cb]);
     }
+    // Keep about ten transposing reads in flight ahead of the products (two per product),
+    // so the LDS latency is covered; left to itself the scheduler may issue each product
+    // right behind its own two reads when register pressure around the call is high.
+    constexpr int READS = 8 * C::CB, MF = 4 * C::CB, AHEAD = 10, PAIRS = (READS - AHEAD) / 2;
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+    for (int k = 0; k < PAIRS; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, MF - PAIRS, 0);
 }
 
 template <int D, bool F8>

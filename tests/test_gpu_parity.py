@@ -71,6 +71,50 @@ def test_fwd_small(fa, B, H, N, d, causal, layout, scale):
     assert_close("LSE", lse, L_ref, TOL_LSE)
 
 
+# More query blocks (of 256 rows) than the GPU has compute units, so the grid runs in
+# several waves of workgroups and the block-to-XCD remapping spans all of them. Every head
+# is checked on the first and last row of every 128-row block (plus random rows), so a
+# block that no workgroup took, or one computed with another block's rows, fails.
+PERSISTENT_CASES = [
+    # B, H, N, causal, layout
+    (1, 33, 2048, True, "bhnd"),
+    (3, 11, 2100, False, "bnhd"),
+    (2, 40, 1800, True, "bnhd"),
+]
+
+
+@pytest.mark.parametrize("B,H,N,causal,layout", PERSISTENT_CASES)
+def test_fwd_more_blocks_than_compute_units(fa, B, H, N, causal, layout):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert B * H * ((N + 255) // 256) > cus, "the case must exceed the compute-unit count"
+    x = small_inputs(B, H, N, 128, layout, seed=B * H + N)
+    sc = scale_for(128)
+    q, k, v = (to_dev(x[n]) for n in "qkv")
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    rows = sample_rows(N, 128, np.random.default_rng(N), extra=8)
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    O_ref, L_ref = oracle.attention_forward(x["q"], x["k"], x["v"], causal=causal, scale=sc, rows=rows,
+                                            heads=heads)
+    for (b, h) in heads:
+        assert_close(f"O[{b},{h}]", o[b, h, rows], O_ref[b, h, rows], TOL_OUT)
+        assert_close(f"LSE[{b},{h}]", lse[b, h, rows], L_ref[b, h, rows], TOL_LSE)
+
+
+@pytest.mark.parametrize("key", ["causal_h32_n32k", "causal_b4h32_n4k_bnhd"])
+def test_fwd_workload_writes_every_row(fa, key):
+    """Outputs pre-filled with NaN: after the call no row of any head may still hold it."""
+    w = W.WORKLOADS[key]
+    x = W.make_inputs(w)
+    q, k, v = (to_dev(x[n]) for n in "qkv")
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((w.B, w.H, w.N), float("nan"), dtype=torch.float32, device="cuda")
+    fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any().item()
+    assert torch.isfinite(lse).all().item()
+
+
 def test_fwd_empty_is_noop(fa):
     q = torch.zeros((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
     o, lse = fa.fwd(q, q, q, causal=True)
