@@ -34,6 +34,12 @@ int ok() {
 }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;   // B, H, N each stay well inside int32
+// Query rows of one call (B*H*N, or H*total when packed): every launch then stays below 2^31
+// work-items (the backward's dK/dV grid has four per key row) and its workgroup indices in int.
+constexpr int64_t kMaxRowsFwd = (int64_t)1 << 30;
+constexpr int64_t kMaxRowsBwd = (int64_t)1 << 29;
+// Token stride in elements: the tile loaders address a 64-row tile with 32-bit byte offsets.
+constexpr int64_t kMaxRowStride = (int64_t)1 << 24;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -55,6 +61,9 @@ int check_tensor(const char* name, const void* p, const fa_strides& s, int mult 
         return fail(FA_ERR_LAYOUT, "%s strides (%lld, %lld, %lld) are not multiples of %d elements", name,
                     (long long)s.b, (long long)s.h, (long long)s.n, mult);
     if (s.b < 0 || s.h < 0 || s.n < 0) return fail(FA_ERR_LAYOUT, "%s has a negative stride", name);
+    if (s.n > kMaxRowStride)
+        return fail(FA_ERR_LAYOUT, "%s token stride %lld exceeds %lld elements", name, (long long)s.n,
+                    (long long)kMaxRowStride);
     return FA_OK;
 }
 
@@ -93,6 +102,10 @@ int check_desc(const fa_attn_desc* dp, bool backward) {
         return fail(FA_ERR_SHAPE, "bad packed row count total=%lld", (long long)d.total);
     if (packed(d) && d.total * d.H > kMaxDim)
         return fail(FA_ERR_SHAPE, "H * total too large (%lld * %lld)", (long long)d.H, (long long)d.total);
+    const int64_t rows = packed(d) ? d.H * d.total : d.B * d.H * d.N;
+    const int64_t max_rows = backward ? kMaxRowsBwd : kMaxRowsFwd;
+    if (rows > max_rows)
+        return fail(FA_ERR_SHAPE, "%lld query rows in one call exceed %lld", (long long)rows, (long long)max_rows);
     if (!std::isfinite(d.scale)) return fail(FA_ERR_ARG, "scale is not finite");
     if (d.dtype != FA_DTYPE_BF16 && d.dtype != FA_DTYPE_FP8_E4M3) return fail(FA_ERR_ARG, "unknown dtype %d", d.dtype);
     if (d.dtype == FA_DTYPE_FP8_E4M3) {

@@ -92,24 +92,28 @@ __global__ __launch_bounds__(kThreads) void pre_kernel(const uint16_t* o, int64_
     constexpr int LPR = D / 8;                       // lanes per row, 8 elements each
     constexpr int RPB = kThreads / LPR;              // rows per block
     const int tid = threadIdx.x;
-    const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;
     const int part = tid % LPR;
-    float acc = 0.0f;
-    if (row < rows) {
-        const int64_t bh = row / N;
-        const int n = (int)(row % N);
-        const int b = (int)(bh / H), h = (int)(bh % H);
-        const u32x4 x = *reinterpret_cast<const u32x4*>(o + b * osb + h * osh + (int64_t)n * osn + 8 * part);
-        const u32x4 y = *reinterpret_cast<const u32x4*>(dout + b * dsb + h * dsh + (int64_t)n * dsn + 8 * part);
+    // Grid-stride over blocks of RPB rows: the launch caps the grid, so any row count stays
+    // within one launch. The loop bound depends only on the block index (uniform per block).
+    for (int64_t r0 = (int64_t)blockIdx.x * RPB; r0 < rows; r0 += (int64_t)gridDim.x * RPB) {
+        const int64_t row = r0 + tid / LPR;
+        float acc = 0.0f;
+        if (row < rows) {
+            const int64_t bh = row / N;
+            const int n = (int)(row % N);
+            const int b = (int)(bh / H), h = (int)(bh % H);
+            const u32x4 x = *reinterpret_cast<const u32x4*>(o + b * osb + h * osh + (int64_t)n * osn + 8 * part);
+            const u32x4 y = *reinterpret_cast<const u32x4*>(dout + b * dsb + h * dsh + (int64_t)n * dsn + 8 * part);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            acc += __uint_as_float(x[w] << 16) * __uint_as_float(y[w] << 16);
-            acc += __uint_as_float(x[w] & 0xffff0000u) * __uint_as_float(y[w] & 0xffff0000u);
+            for (int w = 0; w < 4; ++w) {
+                acc += __uint_as_float(x[w] << 16) * __uint_as_float(y[w] << 16);
+                acc += __uint_as_float(x[w] & 0xffff0000u) * __uint_as_float(y[w] & 0xffff0000u);
+            }
         }
-    }
 #pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-    if (row < rows && part == 0) delta[row] = acc;
+        for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+        if (row < rows && part == 0) delta[row] = acc;
+    }
 }
 
 // ----------------------------------------------------------------------------- dK, dV
@@ -628,7 +632,8 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
         const int Np = packed ? (int)L.total : L.N;
         const int64_t rows = (int64_t)Bp * L.H * Np;
         constexpr int RPB = kThreads / (D / 8);
-        const int64_t grid = (rows + RPB - 1) / RPB;
+        constexpr int64_t kMaxGrid = (int64_t)1 << 16;   // the kernel strides over the rest
+        const int64_t grid = std::min((rows + RPB - 1) / RPB, kMaxGrid);
         hipLaunchKernelGGL((pre_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                            static_cast<const uint16_t*>(a.o.p), packed ? 0 : a.o.sb, a.o.sh, a.o.sn,
                            static_cast<const uint16_t*>(a.dout.p), packed ? 0 : a.dout.sb, a.dout.sh, a.dout.sn,

@@ -16,7 +16,12 @@
  * [num_heads, N, d] in page 1's CUDA kernel, (B, T, H, D_head) in "How to Use Flash MSA
  * Kernels for Long Context", section "Step-by-Step"). Requirements (else FA_ERR_LAYOUT):
  * the head dimension is contiguous; every pointer is 16-byte aligned; every stride is a
- * multiple of 8 elements. LSE is fp32, contiguous [B, H, N], natural logarithm.
+ * multiple of 8 elements and non-negative; the token stride (stride.n) is at most 2^24
+ * elements. LSE is fp32, contiguous [B, H, N], natural logarithm.
+ *
+ * Sizes (else FA_ERR_SHAPE): B, H, N (and H_kv, packed total) at most 2^30 each, B*H at
+ * most 2^30, and at most 2^30 query rows (B*H*N, or H*total when packed) per forward call,
+ * 2^29 per backward call; the kernels index workgroups and grids with 32-bit integers.
  *
  * Ownership and execution. The caller allocates and owns every buffer (device memory for
  * tensors, lists and workspace; host memory only where a parameter says "host"). The
@@ -49,9 +54,9 @@ extern "C" {
 
 #define FA_OK 0
 #define FA_ERR_NULL 1       /* a required pointer is NULL                                 */
-#define FA_ERR_SHAPE 2      /* B, H or N negative; sparse block size unsupported            */
+#define FA_ERR_SHAPE 2      /* B, H or N negative or too large; sparse block size unsupported */
 #define FA_ERR_HEADDIM 3    /* d is not 64 or 128                                           */
-#define FA_ERR_LAYOUT 4     /* d not contiguous, pointer or stride not 16-byte aligned      */
+#define FA_ERR_LAYOUT 4     /* pointer or stride not 16-byte aligned, token stride > 2^24    */
 #define FA_ERR_LIST 5       /* block lists fail fa_check_block_lists (host checks only)     */
 #define FA_ERR_WORKSPACE 6  /* backward workspace missing or too small                      */
 #define FA_ERR_HIP 7        /* HIP runtime error (no device, launch failure, ...)           */

@@ -71,6 +71,9 @@ def test_fwd_argument_errors_before_any_hip_call(fa):
     assert call_fwd(fa, d=96) == 3                   # FA_ERR_HEADDIM
     assert call_fwd(fa, q=24) == 4                   # misaligned pointer -> FA_ERR_LAYOUT
     assert call_fwd(fa, st=(8192, 8192, 100)) == 4   # stride not a multiple of 8
+    assert call_fwd(fa, st=(1 << 30, 1 << 30, 1 << 25)) == 4   # token stride past 32-bit tile offsets
+    assert "token stride" in fa.lib.fa_last_error().decode()
+    assert call_fwd(fa, B=2, H=1 << 10, N=(1 << 19) + 64) == 2   # more than 2^30 query rows
     assert call_fwd(fa, scale=float("inf")) == 8     # FA_ERR_ARG
     assert "scale" in fa.lib.fa_last_error().decode()
     assert call_fwd(fa, q=0, N=0) == 0               # empty problem: OK, nothing launched
@@ -225,6 +228,10 @@ def test_attn_bwd_argument_errors(fa):
     assert "q_offsets" in fa.lib.fa_last_error().decode()
     assert call_attn_bwd(fa, make_desc(fa, q_offsets=16, **sparse)) == 1
     assert call_attn_bwd(fa, make_desc(fa), ws=0) == 6
+    # more than 2^29 query rows in one backward call (the forward takes up to 2^30)
+    assert call_attn_bwd(fa, make_desc(fa, B=1, H=1 << 10, H_kv=1 << 10, N=(1 << 19) + 64)) == 2
+    assert "query rows" in fa.lib.fa_last_error().decode()
+    assert call_attn_bwd(fa, make_desc(fa, H=1 << 10, H_kv=1 << 10, N=1, cu_seqlens=16, total=(1 << 19) + 64)) == 2
     assert call_attn_bwd(fa, make_desc(fa), ws_bytes=100) == 6
 
 
