@@ -482,6 +482,230 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_kernel(Params p) {
                     p.lse + seq_stat_off(sp, b, hh, p.H, p.N, p.total), qrow, N, hf, p.vdesc);
 }
 
+// ----------------------------------------------------------------------------- dense, ping-pong,
+// tiles loaded straight into LDS (bf16, head dimension 128)
+//
+// Same phases as fwd_pingpong_kernel, but the K and V tiles travel from memory to LDS with
+// buffer loads that write LDS directly (no staging registers, no LDS store instructions).
+// One such load writes 16 bytes per lane at consecutive addresses, i.e. four whole 256-byte
+// rows per wave instruction, so the tiles are kept unpadded and conflicts are avoided by
+// placing 16-byte chunk c of row r at chunk slot c ^ swz(r) instead:
+// * K (16-byte row reads, 16 rows per pass): swz(r) = r & 15;
+// * V (transposing reads, four rows x four chunks per 32 lanes): swz(r) = 4 * (r & 3).
+// Each lane loads the chunk that belongs at its slot, so the rows are still read whole.
+// Four LDS stages; the loads of step m + 2 are issued at the start of phase 2m (into the
+// stage of step m - 2, last read in phase 2m - 1) and have four phases to arrive.
+// The loads are issued from inline assembly: the compiler then does not treat them as
+// pending LDS stores, which would make every barrier wait for all of them; the waits are
+// placed by hand (an odd phase ends with vmcnt(4): only the latest step may be in flight).
+constexpr int kDmaBufs = 4;
+constexpr int kDmaRowB = 256;                    // bytes per bf16 row at head dimension 128
+constexpr int kDmaTileB = kBK * kDmaRowB;        // 16 KB per tile
+constexpr int kDmaStageB = 2 * kDmaTileB;        // K then V
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor words over [base, base + bytes) (as make_rsrc), for inline assembly.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = (int)(uint32_t)a;
+    r[1] = (int)((uint32_t)(a >> 32) & 0xffffu);
+    r[2] = (int)bytes;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from the buffer at byte offset `voff` into LDS at `lds` + 16 * lane.
+__device__ __forceinline__ void load16_to_lds(i32x4 r, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(r), "s"(lds)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ int swz_k(int row) { return row & 15; }
+__device__ __forceinline__ int swz_v(int row) { return 4 * (row & 3); }
+
+// Per-thread part of one step's loads: two 1 KB pieces (four rows) of K and two of V per wave.
+struct DmaStage {
+    uint32_t koff[2], voff[2];   // global byte offsets relative to the step's first row
+
+    __device__ void init(int wave, int lane, int64_t ksn, int64_t vsn) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = 4 * (2 * wave + j) + (lane >> 4), slot = lane & 15;
+            koff[j] = (uint32_t)((int64_t)row * ksn * 2 + 16 * (slot ^ swz_k(row)));
+            voff[j] = (uint32_t)((int64_t)row * vsn * 2 + 16 * (slot ^ swz_v(row)));
+        }
+    }
+    __device__ void issue(const uint16_t* kbase, const uint16_t* vbase, int64_t ksn, int64_t vsn, int kt0, int N,
+                          uint32_t stage, int wave) const {
+        const i32x4 rk = rsrc_words(kbase + (int64_t)kt0 * ksn, rows_bytes(kt0, N, ksn, 128, kBK));
+        const i32x4 rv = rsrc_words(vbase + (int64_t)kt0 * vsn, rows_bytes(kt0, N, vsn, 128, kBK));
+        const uint32_t piece = stage + 2048u * (uint32_t)wave;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) load16_to_lds(rk, koff[j], piece + 1024u * j);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) load16_to_lds(rv, voff[j], piece + kDmaTileB + 1024u * j);
+    }
+};
+
+// Per-lane byte offsets (within a stage) of the swizzled reads.
+struct DmaAddr {
+    uint32_t k[8];   // K: row i, logical chunk 2 * ks + hf (the second 32-key block is +8 KB)
+    uint32_t v[4];   // V (transposing reads): per 32-column block cb
+
+    __device__ void init(int i, int hf) {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) k[ks] = (uint32_t)(i * kDmaRowB + 16 * ((2 * ks + hf) ^ swz_k(i)));
+        const int g16 = (i >> 4) & 1, j16 = i & 15;
+        const int row = 4 * hf + (j16 >> 2);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const int chunk = 4 * cb + 2 * g16 + ((j16 & 3) >> 1);
+            v[cb] = (uint32_t)(kDmaTileB + row * kDmaRowB + 16 * (chunk ^ swz_v(row)) + 8 * (j16 & 1));
+        }
+    }
+};
+
+__device__ __forceinline__ const bf16x8& lds16(const unsigned char* base, uint32_t off) {
+    return *reinterpret_cast<const bf16x8*>(base + off);
+}
+
+// S^T = K Q^T for one 64-key step from a swizzled stage (same products as scores()).
+__device__ __forceinline__ void scores_sw(const unsigned char* st, Rows<128, false>& w, const DmaAddr& a) {
+    w.s[0] = f32x16{};
+    w.s[1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            w.s[kb] = mfma32(lds16(st, a.k[ks] + 32 * kDmaRowB * kb), w.qf.v[ks], w.s[kb]);
+    constexpr int N = 16, AHEAD = 6;
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+    for (int k = 0; k < N - AHEAD; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
+// O^T += V^T P^T from a swizzled stage (same products and operand layout as pv()).
+__device__ __forceinline__ void pv_sw(const unsigned char* st, Rows<128, false>& w, const DmaAddr& a) {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        bf16x8 op[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const unsigned char* p0 = st + a.v[cb] + (32 * kb + 16 * s2) * kDmaRowB;
+                const u32x2 lo = lds_read_tr4(reinterpret_cast<const uint16_t*>(p0));
+                const u32x2 hi = lds_read_tr4(reinterpret_cast<const uint16_t*>(p0 + 8 * kDmaRowB));
+                u32x4 x;
+                x[0] = lo[0]; x[1] = lo[1]; x[2] = hi[0]; x[3] = hi[1];
+                op[kb][s2] = as_bf16x8(x);
+            }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) w.o[cb] = mfma32(op[kb][s2], w.pb[kb][s2], w.o[cb]);
+    }
+    constexpr int READS = 32, MF = 16, AHEAD = 10, PAIRS = (READS - AHEAD) / 2;
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+    for (int k = 0; k < PAIRS; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, MF - PAIRS, 0);
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_dma_kernel(Params p) {
+    constexpr int D = 128;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kDmaBufs * kDmaStageB];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, i = lane & 31;
+    const int role = wave >> 2;   // group 1 runs one phase behind group 0
+
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = logical / p.nqb;
+    int qblk = logical % p.nqb;
+    if (CAUSAL) qblk = p.nqb - 1 - qblk;   // longest query blocks first
+    const int hh = bh / p.B, b = bh % p.B;   // head-major: an XCD's share spans every sequence
+    const SeqSpan sp = seq_span(p.cu, p.total, b, p.N);
+    const int N = sp.len;
+    const int q0 = qblk * kPPRows;
+    if (q0 >= N) return;   // past the end of a shorter packed sequence (uniform per workgroup)
+
+    const int hk = hh / p.G;
+    const uint16_t* kp = static_cast<const uint16_t*>(p.k) + seq_off(sp, b, hk, p.ksb, p.ksh, p.ksn);
+    const uint16_t* vp = static_cast<const uint16_t*>(p.v) + seq_off(sp, b, hk, p.vsb, p.vsh, p.vsn);
+
+    const int qw0 = q0 + 32 * wave;
+    const int qrow = qw0 + i;
+    const int qlast = min(q0 + kPPRows - 1, N - 1);
+
+    Rows<D, false> w;
+    load_q<D, false>(w, static_cast<const uint16_t*>(p.q) + seq_off(sp, b, hh, p.qsb, p.qsh, p.qsn), p.qsn, qrow,
+                     N, hf);
+
+    int T = (N + kBK - 1) / kBK;
+    if (CAUSAL) T = min(T, qlast / kBK + 1);
+    const int Tw = CAUSAL ? min(T, (qw0 + 31) / kBK + 1) : T;
+    const bool rows_valid = qw0 < N;
+    const float c = p.c;
+    const bool cpos = c >= 0.0f;
+
+    DmaStage st;
+    st.init(wave, lane, p.ksn, p.vsn);
+    DmaAddr ad;
+    ad.init(i, hf);
+    // the wave index and the LDS base are uniform: keep them in scalar registers (the loads
+    // take their LDS address from M0)
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem);
+    if (T > 0) st.issue(kp, vp, p.ksn, p.vsn, 0, N, lds0, wave_u);
+    if (T > 1) st.issue(kp, vp, p.ksn, p.vsn, kBK, N, lds0 + kDmaStageB, wave_u);
+    // Settle every outstanding load (Q fragments and the first two steps) before the loop.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // Phase ph: group g works on local phase lp = ph - g. Even lp = 2t: P.V of step t-1 and
+    // S of step t (MFMA); odd lp = 2t+1: softmax of step t (VALU).
+    for (int ph = 0; ph < 2 * T + 2; ++ph) {
+        if ((ph & 1) == 0) {
+            const int s2 = (ph >> 1) + 2;
+            if (s2 < T) st.issue(kp, vp, p.ksn, p.vsn, s2 * kBK, N, lds0 + (s2 % kDmaBufs) * kDmaStageB, wave_u);
+        }
+        const int lp = ph - role;
+        if (lp >= 0 && rows_valid) {
+            const int t = lp >> 1;
+            if ((lp & 1) == 0) {
+                __builtin_amdgcn_s_setprio(1);
+                if (t >= 1 && t - 1 < Tw) pv_sw(smem + ((t - 1) % kDmaBufs) * kDmaStageB, w, ad);
+                if (t < Tw) scores_sw(smem + (t % kDmaBufs) * kDmaStageB, w, ad);
+                __builtin_amdgcn_s_setprio(0);
+            } else if (t < Tw) {
+                const int kt = t * kBK;
+                const bool masked = (kt + kBK > N) || (CAUSAL && kt + kBK - 1 > qw0);
+                softmax<D, false, CAUSAL>(w, masked, kt, qrow, N, c, cpos, hf);
+            }
+        }
+        // After an odd phase the next one reads the step loaded two phase pairs ago: wait
+        // until only the latest step's four loads of this wave may still be in flight.
+        if (ph & 1) __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4), other counters unrestricted
+        __syncthreads();
+    }
+    epilogue<D, false>(w, p.o + seq_off(sp, b, hh, p.osb, p.osh, p.osn), p.osn,
+                       p.lse + seq_stat_off(sp, b, hh, p.H, p.N, p.total), qrow, N, hf, p.vdesc);
+}
+
 // ----------------------------------------------------------------------------- sparse
 constexpr int kSpThreads = 256;   // 4 waves, one 128-row block
 
@@ -589,7 +813,10 @@ hipError_t dispatch(Params p, bool sparse, hipStream_t stream) {
     }
     p.nqb = (p.N + kPPRows - 1) / kPPRows;
     const int64_t grid = (int64_t)p.B * p.H * p.nqb;
-    hipLaunchKernelGGL((fwd_pingpong_kernel<D, CAUSAL, F8>), dim3((unsigned)grid), dim3(kPPThreads), 0, stream, p);
+    if constexpr (D == 128 && !F8)
+        hipLaunchKernelGGL((fwd_pingpong_dma_kernel<CAUSAL>), dim3((unsigned)grid), dim3(kPPThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fwd_pingpong_kernel<D, CAUSAL, F8>), dim3((unsigned)grid), dim3(kPPThreads), 0, stream, p);
     return hipGetLastError();
 }
 
