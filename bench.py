@@ -329,7 +329,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(), "algorithmic_bytes": head["bytes"],
-                     "kernel": "fwd_pingpong_kernel<128, causal>", "per_launch_flop": head["flops"],
+                     "kernel": "fwd_pingpong_dma_kernel<causal>", "per_launch_flop": head["flops"],
                      "avg_launch_ms": round(t["mean_ms"], 4)},
         "cpu_baseline": cpu,
         "workloads": others,
