@@ -527,27 +527,32 @@ __device__ __forceinline__ void load16_to_lds(i32x4 r, uint32_t voff, uint32_t l
 __device__ __forceinline__ int swz_k(int row) { return row & 15; }
 __device__ __forceinline__ int swz_v(int row) { return 4 * (row & 3); }
 
-// Per-thread part of one step's loads: two 1 KB pieces (four rows) of K and two of V per wave.
+// Per-thread part of one step's loads: a 64-row tile is 16 pieces of 1 KB (four rows each);
+// each of the NW waves loads 16 / NW consecutive pieces of K and as many of V.
+template <int NW>
 struct DmaStage {
-    uint32_t koff[2], voff[2];   // global byte offsets relative to the step's first row
+    static constexpr int P = 16 / NW;
+    static_assert(P * NW == 16, "the waves must split the tile evenly");
+    uint32_t koff[P], voff[P];   // global byte offsets relative to the step's first row
 
     __device__ void init(int wave, int lane, int64_t ksn, int64_t vsn) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = 4 * (2 * wave + j) + (lane >> 4), slot = lane & 15;
+        for (int j = 0; j < P; ++j) {
+            const int row = 4 * (P * wave + j) + (lane >> 4), slot = lane & 15;
             koff[j] = (uint32_t)((int64_t)row * ksn * 2 + 16 * (slot ^ swz_k(row)));
             voff[j] = (uint32_t)((int64_t)row * vsn * 2 + 16 * (slot ^ swz_v(row)));
         }
     }
+    // `stage` (LDS byte address) and `wave` must be wave-uniform: the loads take M0.
     __device__ void issue(const uint16_t* kbase, const uint16_t* vbase, int64_t ksn, int64_t vsn, int kt0, int N,
                           uint32_t stage, int wave) const {
         const i32x4 rk = rsrc_words(kbase + (int64_t)kt0 * ksn, rows_bytes(kt0, N, ksn, 128, kBK));
         const i32x4 rv = rsrc_words(vbase + (int64_t)kt0 * vsn, rows_bytes(kt0, N, vsn, 128, kBK));
-        const uint32_t piece = stage + 2048u * (uint32_t)wave;
+        const uint32_t piece = stage + 1024u * P * (uint32_t)wave;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) load16_to_lds(rk, koff[j], piece + 1024u * j);
+        for (int j = 0; j < P; ++j) load16_to_lds(rk, koff[j], piece + 1024u * j);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) load16_to_lds(rv, voff[j], piece + kDmaTileB + 1024u * j);
+        for (int j = 0; j < P; ++j) load16_to_lds(rv, voff[j], piece + kDmaTileB + 1024u * j);
     }
 };
 
@@ -661,7 +666,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_dma_kernel(Params 
     const float c = p.c;
     const bool cpos = c >= 0.0f;
 
-    DmaStage st;
+    DmaStage<kPPThreads / 64> st;
     st.init(wave, lane, p.ksn, p.vsn);
     DmaAddr ad;
     ad.init(i, hf);
@@ -803,12 +808,108 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
                     p.lse + seq_stat_off(sp, b, hh, p.H, p.N, p.total), qrow, N, hf, p.vdesc);
 }
 
+// Block-sparse forward, bf16 at head dimension 128, with the K/V tiles loaded straight into
+// LDS in the swizzled layout of fwd_pingpong_dma_kernel: two 32 KB stages per workgroup (two
+// workgroups per CU); the loads of the next listed step are issued at the start of a step
+// into the other stage and waited for (vmcnt(0)) before the step's closing barrier.
+template <bool CAUSAL>
+__global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_dma_kernel(Params p) {
+    constexpr int D = 128;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kDmaStageB];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, i = lane & 31;
+
+    // Plain order, longest lists first (as fwd_sparse_kernel).
+    const int bh = blockIdx.x / p.nqb;
+    const int qblk = p.nqb - 1 - blockIdx.x % p.nqb;
+    const int hh = bh / p.B, b = bh % p.B;
+    const SeqSpan sp = seq_span(p.cu, p.total, b, p.N);
+    const int N = sp.len;
+    const int q0 = qblk * kSparseBlock;
+    if (q0 >= N) return;
+
+    const int hk = hh / p.G;
+    const uint16_t* kp = static_cast<const uint16_t*>(p.k) + seq_off(sp, b, hk, p.ksb, p.ksh, p.ksn);
+    const uint16_t* vp = static_cast<const uint16_t*>(p.v) + seq_off(sp, b, hk, p.vsb, p.vsh, p.vsn);
+
+    const int qw0 = q0 + 32 * wave;
+    const int qrow = qw0 + i;
+    const int qlast = min(q0 + kSparseBlock - 1, N - 1);
+
+    Rows<D, false> w;
+    load_q<D, false>(w, static_cast<const uint16_t*>(p.q) + seq_off(sp, b, hh, p.qsb, p.qsh, p.qsn), p.qsn, qrow,
+                     N, hf);
+
+    const int nkb = (N + kSparseBlock - 1) / kSparseBlock;
+    int64_t lo = load_uniform(p.kv_offsets, qblk), hi = load_uniform(p.kv_offsets, qblk + 1);
+    lo = lo < 0 ? 0 : (lo > p.nnz ? p.nnz : lo);
+    hi = hi < lo ? lo : (hi > p.nnz ? p.nnz : hi);
+    int t = (int)(2 * lo);
+    const int t_end = (int)(2 * hi);
+    auto step_key = [&](int tt) -> int {   // first key of step tt, or -1 to skip it
+        const int kblk = load_uniform(p.kv_indices, tt >> 1);
+        if (kblk < 0 || kblk >= nkb || (CAUSAL && kblk > qblk)) return -1;
+        const int kt0 = kblk * kSparseBlock + (tt & 1) * kBK;
+        if (kt0 >= N || (CAUSAL && kt0 > qlast)) return -1;
+        return kt0;
+    };
+    int kt = -1;
+    while (t < t_end && (kt = step_key(t)) < 0) ++t;
+
+    const float c = p.c;
+    const bool cpos = c >= 0.0f;
+
+    DmaStage<kSpThreads / 64> st;
+    st.init(wave, lane, p.ksn, p.vsn);
+    DmaAddr ad;
+    ad.init(i, hf);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem);
+    if (t < t_end) st.issue(kp, vp, p.ksn, p.vsn, kt, N, lds0, wave_u);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    int cur = 0;
+    while (t < t_end) {
+        int tn = t + 1, ktn = -1;
+        while (tn < t_end && (ktn = step_key(tn)) < 0) ++tn;
+        const bool has_next = tn < t_end;
+        // the other stage was last read in the previous step, which ended with a barrier
+        if (has_next) st.issue(kp, vp, p.ksn, p.vsn, ktn, N, lds0 + (cur ^ 1) * kDmaStageB, wave_u);
+
+        const unsigned char* buf = smem + cur * kDmaStageB;
+        if (qw0 < N && (!CAUSAL || kt <= qw0 + 31)) {
+            const bool masked = (kt + kBK > N) || (CAUSAL && kt + kBK - 1 > qw0);
+            __builtin_amdgcn_s_setprio(1);
+            scores_sw(buf, w, ad);
+            __builtin_amdgcn_s_setprio(0);
+            softmax<D, false, CAUSAL>(w, masked, kt, qrow, N, c, cpos, hf);
+            __builtin_amdgcn_s_setprio(1);
+            pv_sw(buf, w, ad);
+            __builtin_amdgcn_s_setprio(0);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of the next step
+        __syncthreads();
+        cur ^= 1;
+        t = tn;
+        kt = ktn;
+    }
+    epilogue<D, false>(w, p.o + seq_off(sp, b, hh, p.osb, p.osh, p.osn), p.osn,
+                       p.lse + seq_stat_off(sp, b, hh, p.H, p.N, p.total), qrow, N, hf, p.vdesc);
+}
+
 template <int D, bool CAUSAL, bool F8>
 hipError_t dispatch(Params p, bool sparse, hipStream_t stream) {
     if (sparse) {
         p.nqb = (p.N + kSparseBlock - 1) / kSparseBlock;
         const int64_t grid = (int64_t)p.B * p.H * p.nqb;
-        hipLaunchKernelGGL((fwd_sparse_kernel<D, CAUSAL, F8>), dim3((unsigned)grid), dim3(kSpThreads), 0, stream, p);
+        if constexpr (D == 128 && !F8)
+            hipLaunchKernelGGL((fwd_sparse_dma_kernel<CAUSAL>), dim3((unsigned)grid), dim3(kSpThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((fwd_sparse_kernel<D, CAUSAL, F8>), dim3((unsigned)grid), dim3(kSpThreads), 0, stream,
+                               p);
         return hipGetLastError();
     }
     p.nqb = (p.N + kPPRows - 1) / kPPRows;
