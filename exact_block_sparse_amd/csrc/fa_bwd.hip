@@ -621,6 +621,188 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(QParams p) {
     }
 }
 
+// dQ at head dimension 128 with the K/V tiles loaded straight into LDS: one copy of K, with
+// the swizzle that serves both its row reads (S^T) and its transposing reads (dQ^T), and V;
+// two 32 KB stages (two workgroups still fit on a CU). The next step's loads are issued at
+// the start of a step into the other stage and waited for before the step's closing barrier.
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void dq_dma_kernel(QParams p) {
+    constexpr int D = 128;
+    using C = BCfg<D>;
+    constexpr int KSTEPS = C::KSTEPS, CB = C::CB;
+    constexpr int STAGEB = 2 * kLdsTileB;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGEB];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, i = lane & 31;
+    // Block-sparse: plain order, so that all XCDs work on the same head at once and its K/V
+    // stay in the cache they share (strided lists reach back over the whole head).
+    const int logical = p.kv_offsets ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = logical / p.nqb;
+    int qb = logical % p.nqb;
+    if (CAUSAL) qb = p.nqb - 1 - qb;
+    const int hh = bh / p.B, b = bh % p.B;   // head-major: an XCD's share spans every sequence
+    const SeqSpan sp = seq_span(p.cu, p.total, b, p.N);
+    const int N = sp.len;
+    const int q0 = qb * kQ_BQ;
+    if (q0 >= N) return;   // past the end of a shorter packed sequence (uniform per workgroup)
+
+    const int hk = hh / p.G;
+    const uint16_t* kp = p.k + seq_off(sp, b, hk, p.ksb, p.ksh, p.ksn);
+    const uint16_t* vp = p.v + seq_off(sp, b, hk, p.vsb, p.vsh, p.vsn);
+    const int qw0 = q0 + 32 * wave;
+    const int qrow = qw0 + i;
+    const int qlast = min(q0 + kQ_BQ - 1, N - 1);
+
+    bf16x8 qf[KSTEPS], df[KSTEPS];
+    {
+        const uint16_t* qr = p.q + seq_off(sp, b, hh, p.qsb, p.qsh, p.qsn) + (int64_t)qrow * p.qsn + 8 * hf;
+        const uint16_t* dr = p.dout + seq_off(sp, b, hh, p.dsb, p.dsh, p.dsn) + (int64_t)qrow * p.dsn + 8 * hf;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            qf[ks] = as_bf16x8(load16(qr + 16 * ks, qrow < N));
+            df[ks] = as_bf16x8(load16(dr + 16 * ks, qrow < N));
+        }
+    }
+    const int64_t so = seq_stat_off(sp, b, hh, p.H, p.N, p.total);
+    float lse2 = 0.0f, dlt = 0.0f;
+    if (qrow < N) {
+        float l = p.lse[so + qrow];
+        if (l == -__builtin_inff()) l = __builtin_inff();
+        lse2 = l * kLog2e;
+        dlt = p.delta[so + qrow];
+    }
+
+    f32x16 dq[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) dq[cb] = f32x16{};
+
+    // Steps: 64-key tiles. Dense: from 0 to the end (causal: to the block's last row).
+    // Block-sparse: both halves of every key block listed for this query block; entries out
+    // of range (or, causal, above the diagonal) are skipped.
+    int nsteps = (N + kStep - 1) / kStep;
+    if (CAUSAL) nsteps = min(nsteps, qlast / kStep + 1);
+    const bool sparse = p.kv_offsets != nullptr;
+    int64_t lo = 0;
+    if (sparse) {
+        int64_t hi = load_uniform(p.kv_offsets, qb + 1);
+        lo = load_uniform(p.kv_offsets, qb);
+        lo = lo < 0 ? 0 : (lo > p.nnz ? p.nnz : lo);
+        hi = hi < lo ? lo : (hi > p.nnz ? p.nnz : hi);
+        nsteps = (int)(2 * (hi - lo));
+    }
+    const int nkb = (N + kQ_BQ - 1) / kQ_BQ;
+    auto step_key = [&](int t) -> int {   // first key of step t, or -1 to skip it
+        if (!sparse) return t * kStep;
+        const int kb = load_uniform(p.kv_indices, lo + (t >> 1));
+        if (kb < 0 || kb >= nkb || (CAUSAL && kb > qb)) return -1;
+        const int kt0 = kb * kQ_BQ + (t & 1) * kStep;
+        return (kt0 < N && (!CAUSAL || kt0 <= qlast)) ? kt0 : -1;
+    };
+    const float c = p.c;
+
+    // Per-lane byte offsets within a stage: row reads of K (V: + kLdsTileB), row i and
+    // logical chunk 2 * ks + hf; transposing reads of K per 32-column block cb, for the
+    // lane's row and the row 8 below it.
+    uint32_t ar[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) ar[ks] = (uint32_t)(i * kLdsRowB + 16 * ((2 * ks + hf) ^ swz<kSwzBoth>(i)));
+    uint32_t at[CB][2];
+    {
+        const int g16 = (lane >> 4) & 1, j16 = lane & 15;
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+            const int row = 4 * hf + (j16 >> 2) + 8 * h8;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const int chunk = 4 * cb + 2 * g16 + ((j16 & 3) >> 1);
+                at[cb][h8] = (uint32_t)(row * kLdsRowB + 16 * (chunk ^ swz<kSwzBoth>(row)) + 8 * (j16 & 1));
+            }
+        }
+    }
+
+    DmaStage<kThreads / 64, kSwzBoth, kSwzBoth> st;
+    st.init(wave, lane, p.ksn, p.vsn);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds0 = lds_address(smem);
+    if (nsteps > 0) {
+        const int kt0 = step_key(0);
+        if (kt0 >= 0) st.issue(kp, vp, p.ksn, p.vsn, kt0, N, lds0, wave_u);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int cur = 0;
+    for (int t = 0; t < nsteps; ++t) {
+        // the other stage was last read in the previous step, which ended with a barrier
+        if (t + 1 < nsteps) {
+            const int ktn = step_key(t + 1);
+            if (ktn >= 0) st.issue(kp, vp, p.ksn, p.vsn, ktn, N, lds0 + (cur ^ 1) * STAGEB, wave_u);
+        }
+        const unsigned char* buf = smem + cur * STAGEB;
+        const int kt = step_key(t);
+        if (kt >= 0 && qw0 < N && (!CAUSAL || kt <= qw0 + 31)) {
+            const bool masked = (kt + kStep > N) || (CAUSAL && kt + kStep - 1 > qw0);
+            bf16x8 db[2][2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                f32x16 sacc = {}, pacc = {};
+                const unsigned char* kr = buf + 32 * kb * kLdsRowB;
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks) {
+                    sacc = mfma32(*reinterpret_cast<const bf16x8*>(kr + ar[ks]), qf[ks], sacc);
+                    pacc = mfma32(*reinterpret_cast<const bf16x8*>(kr + kLdsTileB + ar[ks]), df[ks], pacc);
+                }
+                float dsv[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float pe = fast_exp2(fmaf(sacc[r], c, -lse2));
+                    if (masked) {
+                        const int kk = kt + 32 * kb + acc_row(r, hf);
+                        if (kk >= N || (CAUSAL && kk > qrow)) pe = 0.0f;
+                    }
+                    dsv[r] = pe * (pacc[r] - dlt);
+                }
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+                    db[kb][st] = pack8(dsv[8 * st], dsv[8 * st + 1], dsv[8 * st + 2], dsv[8 * st + 3],
+                                       dsv[8 * st + 4], dsv[8 * st + 5], dsv[8 * st + 6], dsv[8 * st + 7]);
+            }
+            // dQ^T += K^T dS^T
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        const unsigned char* p0 = buf + (32 * kb + 16 * s2) * kLdsRowB;
+                        const u32x2 lo = lds_read_tr4(reinterpret_cast<const uint16_t*>(p0 + at[cb][0]));
+                        const u32x2 hi = lds_read_tr4(reinterpret_cast<const uint16_t*>(p0 + at[cb][1]));
+                        u32x4 x;
+                        x[0] = lo[0]; x[1] = lo[1]; x[2] = hi[0]; x[3] = hi[1];
+                        dq[cb] = mfma32(as_bf16x8(x), db[kb][s2], dq[cb]);
+                    }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of the next step
+        __syncthreads();
+        cur ^= 1;
+    }
+
+    if (qrow < N) {
+        uint16_t* dqr = p.dq + seq_off(sp, b, hh, p.dqsb, p.dqsh, p.dqsn) + (int64_t)qrow * p.dqsn;
+        const float sc = p.scale;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bf16x4 a;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] = (__bf16)(dq[cb][4 * j + e] * sc);
+                *reinterpret_cast<bf16x4*>(dqr + 32 * cb + 8 * j + 4 * hf) = a;
+            }
+    }
+}
+
+
 template <int D, bool CAUSAL>
 hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
     const Layout& L = a.L;
@@ -698,7 +880,10 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
         p.c = c;
         p.scale = a.scale;
         const int64_t grid = (int64_t)L.B * L.H * p.nqb;
-        hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+        if constexpr (D == 128)
+            hipLaunchKernelGGL((dq_dma_kernel<CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
         return hipGetLastError();
     }
 }

@@ -206,4 +206,89 @@ __device__ __forceinline__ const uint16_t* tr_lane_base(const uint16_t* tile, in
     return tile + (4 * hf + (j >> 2)) * stride + 16 * g + 4 * (j & 3);
 }
 
+
+// ----------------------------------------------------------------------------- loads into LDS
+// bf16 tiles of 64 rows at head dimension 128 loaded from memory straight into LDS
+// (`buffer_load_dwordx4 ... lds`: lane L's 16 bytes land at M0 + 16 * L, so one wave
+// instruction fills 1 KB, four whole 256-byte rows). The tiles are unpadded; bank conflicts
+// are avoided by keeping 16-byte chunk c of row r at chunk slot c ^ swz(r), and each lane
+// loads the chunk that belongs at its slot, so every instruction still reads whole rows.
+// Swizzles (all depend on r & 15 only, so 16-row offsets move no chunk):
+// * kSwzRow  = r & 15: 16-byte reads of one chunk by 16 consecutive rows;
+// * kSwzTr   = 4 (r & 3): transposing reads of four consecutive rows x four chunks;
+// * kSwzBoth = 4 (r & 3) | ((r >> 2) & 3): both patterns (a bijection on 16 rows whose bits
+//   2-3 differ between four consecutive rows).
+// The loads are issued from inline assembly so that the compiler does not count them as
+// pending LDS stores (it would make every barrier wait for all of them); callers wait with
+// s_waitcnt vmcnt before the barrier that precedes the first read of a stage.
+constexpr int kLdsRowB = 256;                   // bytes per bf16 row at head dimension 128
+constexpr int kLdsTileB = 64 * kLdsRowB;        // one 64-row tile
+enum { kSwzRow = 0, kSwzTr = 1, kSwzBoth = 2 };
+
+template <int S>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (S == kSwzRow) return row & 15;
+    else if constexpr (S == kSwzTr) return 4 * (row & 3);
+    else return (4 * (row & 3)) | ((row >> 2) & 3);
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor words over [base, base + bytes) (as make_rsrc), for inline assembly.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = (int)(uint32_t)a;
+    r[1] = (int)((uint32_t)(a >> 32) & 0xffffu);
+    r[2] = (int)bytes;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from the buffer at byte offset `voff` into LDS at `lds` + 16 * lane
+// (`lds` wave-uniform). No register receives data, so nothing is left for the compiler to
+// reuse while the load is in flight.
+__device__ __forceinline__ void load16_to_lds(i32x4 r, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(r), "s"(lds)
+                 : "memory", "m0");
+}
+
+// Per-thread part of one step's K and V loads: a 64-row tile is 16 pieces of 1 KB; each of
+// the NW waves loads 16 / NW consecutive pieces of K and as many of V. A stage holds the K
+// tile (swizzle SK) and then the V tile (swizzle SV). Rows past the end read as zeros (the
+// buffer range check).
+template <int NW, int SK, int SV>
+struct DmaStage {
+    static constexpr int P = 16 / NW;
+    static_assert(P * NW == 16, "the waves must split the tile evenly");
+    uint32_t koff[P], voff[P];   // global byte offsets relative to the step's first row
+
+    __device__ void init(int wave, int lane, int64_t ksn, int64_t vsn) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const int row = 4 * (P * wave + j) + (lane >> 4), slot = lane & 15;
+            koff[j] = (uint32_t)((int64_t)row * ksn * 2 + 16 * (slot ^ swz<SK>(row)));
+            voff[j] = (uint32_t)((int64_t)row * vsn * 2 + 16 * (slot ^ swz<SV>(row)));
+        }
+    }
+    // `stage` (LDS byte address) and `wave` must be wave-uniform: the loads take M0.
+    __device__ void issue(const uint16_t* kbase, const uint16_t* vbase, int64_t ksn, int64_t vsn, int r0, int N,
+                          uint32_t stage, int wave) const {
+        const i32x4 rk = rsrc_words(kbase + (int64_t)r0 * ksn, rows_bytes(r0, N, ksn, 128, 64));
+        const i32x4 rv = rsrc_words(vbase + (int64_t)r0 * vsn, rows_bytes(r0, N, vsn, 128, 64));
+        const uint32_t piece = stage + 1024u * P * (uint32_t)wave;
+#pragma unroll
+        for (int j = 0; j < P; ++j) load16_to_lds(rk, koff[j], piece + 1024u * j);
+#pragma unroll
+        for (int j = 0; j < P; ++j) load16_to_lds(rv, voff[j], piece + kLdsTileB + 1024u * j);
+    }
+};
+
+// LDS byte address of a __shared__ object, as a wave-uniform value.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
+}
+
 }  // namespace fa

@@ -499,62 +499,9 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_kernel(Params p) {
 // pending LDS stores, which would make every barrier wait for all of them; the waits are
 // placed by hand (an odd phase ends with vmcnt(4): only the latest step may be in flight).
 constexpr int kDmaBufs = 4;
-constexpr int kDmaRowB = 256;                    // bytes per bf16 row at head dimension 128
-constexpr int kDmaTileB = kBK * kDmaRowB;        // 16 KB per tile
+constexpr int kDmaRowB = kLdsRowB;
+constexpr int kDmaTileB = kLdsTileB;
 constexpr int kDmaStageB = 2 * kDmaTileB;        // K then V
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor words over [base, base + bytes) (as make_rsrc), for inline assembly.
-__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    i32x4 r;
-    r[0] = (int)(uint32_t)a;
-    r[1] = (int)((uint32_t)(a >> 32) & 0xffffu);
-    r[2] = (int)bytes;
-    r[3] = 0x00020000;
-    return r;
-}
-
-// 16 bytes per lane from the buffer at byte offset `voff` into LDS at `lds` + 16 * lane.
-__device__ __forceinline__ void load16_to_lds(i32x4 r, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :
-                 : "v"(voff), "s"(r), "s"(lds)
-                 : "memory", "m0");
-}
-
-__device__ __forceinline__ int swz_k(int row) { return row & 15; }
-__device__ __forceinline__ int swz_v(int row) { return 4 * (row & 3); }
-
-// Per-thread part of one step's loads: a 64-row tile is 16 pieces of 1 KB (four rows each);
-// each of the NW waves loads 16 / NW consecutive pieces of K and as many of V.
-template <int NW>
-struct DmaStage {
-    static constexpr int P = 16 / NW;
-    static_assert(P * NW == 16, "the waves must split the tile evenly");
-    uint32_t koff[P], voff[P];   // global byte offsets relative to the step's first row
-
-    __device__ void init(int wave, int lane, int64_t ksn, int64_t vsn) {
-#pragma unroll
-        for (int j = 0; j < P; ++j) {
-            const int row = 4 * (P * wave + j) + (lane >> 4), slot = lane & 15;
-            koff[j] = (uint32_t)((int64_t)row * ksn * 2 + 16 * (slot ^ swz_k(row)));
-            voff[j] = (uint32_t)((int64_t)row * vsn * 2 + 16 * (slot ^ swz_v(row)));
-        }
-    }
-    // `stage` (LDS byte address) and `wave` must be wave-uniform: the loads take M0.
-    __device__ void issue(const uint16_t* kbase, const uint16_t* vbase, int64_t ksn, int64_t vsn, int kt0, int N,
-                          uint32_t stage, int wave) const {
-        const i32x4 rk = rsrc_words(kbase + (int64_t)kt0 * ksn, rows_bytes(kt0, N, ksn, 128, kBK));
-        const i32x4 rv = rsrc_words(vbase + (int64_t)kt0 * vsn, rows_bytes(kt0, N, vsn, 128, kBK));
-        const uint32_t piece = stage + 1024u * P * (uint32_t)wave;
-#pragma unroll
-        for (int j = 0; j < P; ++j) load16_to_lds(rk, koff[j], piece + 1024u * j);
-#pragma unroll
-        for (int j = 0; j < P; ++j) load16_to_lds(rv, voff[j], piece + kDmaTileB + 1024u * j);
-    }
-};
 
 // Per-lane byte offsets (within a stage) of the swizzled reads.
 struct DmaAddr {
@@ -563,13 +510,13 @@ struct DmaAddr {
 
     __device__ void init(int i, int hf) {
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) k[ks] = (uint32_t)(i * kDmaRowB + 16 * ((2 * ks + hf) ^ swz_k(i)));
+        for (int ks = 0; ks < 8; ++ks) k[ks] = (uint32_t)(i * kDmaRowB + 16 * ((2 * ks + hf) ^ swz<kSwzRow>(i)));
         const int g16 = (i >> 4) & 1, j16 = i & 15;
         const int row = 4 * hf + (j16 >> 2);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             const int chunk = 4 * cb + 2 * g16 + ((j16 & 3) >> 1);
-            v[cb] = (uint32_t)(kDmaTileB + row * kDmaRowB + 16 * (chunk ^ swz_v(row)) + 8 * (j16 & 1));
+            v[cb] = (uint32_t)(kDmaTileB + row * kDmaRowB + 16 * (chunk ^ swz<kSwzTr>(row)) + 8 * (j16 & 1));
         }
     }
 };
@@ -666,15 +613,14 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_dma_kernel(Params 
     const float c = p.c;
     const bool cpos = c >= 0.0f;
 
-    DmaStage<kPPThreads / 64> st;
+    DmaStage<kPPThreads / 64, kSwzRow, kSwzTr> st;
     st.init(wave, lane, p.ksn, p.vsn);
     DmaAddr ad;
     ad.init(i, hf);
     // the wave index and the LDS base are uniform: keep them in scalar registers (the loads
     // take their LDS address from M0)
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem);
+    const uint32_t lds0 = lds_address(smem);
     if (T > 0) st.issue(kp, vp, p.ksn, p.vsn, 0, N, lds0, wave_u);
     if (T > 1) st.issue(kp, vp, p.ksn, p.vsn, kBK, N, lds0 + kDmaStageB, wave_u);
     // Settle every outstanding load (Q fragments and the first two steps) before the loop.
@@ -860,13 +806,12 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_dma_kernel(Params p)
     const float c = p.c;
     const bool cpos = c >= 0.0f;
 
-    DmaStage<kSpThreads / 64> st;
+    DmaStage<kSpThreads / 64, kSwzRow, kSwzTr> st;
     st.init(wave, lane, p.ksn, p.vsn);
     DmaAddr ad;
     ad.init(i, hf);
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem);
+    const uint32_t lds0 = lds_address(smem);
     if (t < t_end) st.issue(kp, vp, p.ksn, p.vsn, kt, N, lds0, wave_u);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
