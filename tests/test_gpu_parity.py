@@ -257,6 +257,38 @@ def test_bwd_small(fa, B, H, N, d, causal, layout):
     assert_close("dV", dv, dV, TOL_OUT)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_packed_qkv_views(fa, causal, d):
+    """Q, K, V as views into one [B, N, 3, H, d] projection buffer: token stride 3*H*d, the
+    three tensors at different offsets of one allocation. Forward and backward."""
+    B, H, N = 2, 3, 333
+    x = small_inputs(B, H, N, d, "bnhd", seed=N + d + causal, grad=True)
+    sc = scale_for(d)
+    qkv = torch.stack([to_dev(x[n]).transpose(1, 2) for n in "qkv"], dim=2).contiguous()   # [B, N, 3, H, d]
+    q, k, v = (qkv[:, :, j].transpose(1, 2) for j in range(3))                            # [B, H, N, d] views
+    assert q.stride(2) == 3 * H * d and k.data_ptr() - q.data_ptr() == H * d * 2
+    do = to_dev(x["do"])
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=sc)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    dQ, dK, dV, O, L = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], causal=causal, scale=sc,
+                                                 return_forward=True)
+    assert_close("O", o, O, TOL_OUT)
+    assert_close("LSE", lse, L, TOL_LSE)
+    assert_close("dQ", dq, dQ, TOL_OUT)
+    assert_close("dK", dk, dK, TOL_OUT)
+    assert_close("dV", dv, dV, TOL_OUT)
+    if causal:   # the block-sparse forward on the same views
+        off, idx = fa.make_block_lists(3, window=1, stride=2)
+        os_, ls = fa.sparse_fwd(q, k, v, off, idx, causal=True, scale=sc)
+        torch.cuda.synchronize()
+        Os, Ls = oracle.attention_forward(x["q"], x["k"], x["v"], causal=True, scale=sc,
+                                          sparse={"block": 128, "window": 1, "stride": 2})
+        assert_close("sparse O", os_, Os, TOL_OUT)
+        assert_close("sparse LSE", ls, Ls, TOL_LSE)
+
+
 def test_bwd_deterministic(fa):
     x = small_inputs(1, 2, 700, 128, seed=9, grad=True)
     q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
