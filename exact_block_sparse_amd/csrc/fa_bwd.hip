@@ -16,16 +16,18 @@
 //    wave's keys stay in registers as MFMA B operands; S = Q K^T and dP = dO V^T read Q and
 //    dO rows from LDS; dV^T += dO^T P and dK^T += Q^T dS read the transposed operands
 //    straight from the row-major tiles with ds_read_b64_tr_b16. dK^T, dV^T accumulate in fp32.
-// 3. dq_kernel: a workgroup owns 128 query rows, as in the forward, and walks the key
-//    tiles: S^T = K Q^T and dP^T = V dO^T with Q and dO in registers, then dQ^T += K^T dS^T
-//    with K^T read transposed from the row-major K tile.
+// 3. dq_dma_kernel (head dimension 128; dq_kernel at 64): a workgroup owns 128 query rows,
+//    as in the forward, and walks the key tiles: S^T = K Q^T and dP^T = V dO^T with Q and dO
+//    in registers, then dQ^T += K^T dS^T with K^T read transposed from the row-major K tile.
 // S and dP are thus computed twice (7 matrix products instead of 5) in exchange for no
 // atomics and bitwise-reproducible results.
 //
-// Every staged tile is written to LDS with plain 16-byte stores, once with a 272-byte row
-// stride (for 16-byte row reads) and, where a transposed operand is needed, once more with
-// a 320-byte stride (for the transposing reads): both access patterns are then free of
-// bank conflicts. Tiles are fetched with raw buffer loads that zero-fill rows past N.
+// LDS layouts, all free of bank conflicts for the reads they serve: the dK/dV kernel stages
+// its Q and dO tiles through registers into one copy with 288-byte rows, which serves both
+// its row reads and its transposing reads; dq_dma_kernel loads K and V straight into LDS as
+// unpadded rows with XOR-swizzled 16-byte chunks (one K copy for both read patterns);
+// dq_kernel keeps a 272-byte row copy and a 320-byte transposed-read copy of K. Tiles are
+// fetched with raw buffer loads that zero-fill rows past N.
 #include "fa_common.h"
 #include "fa_internal.h"
 

@@ -16,11 +16,13 @@
 //   v_mfma_f32_32x32x16_bf16, so the 32 scores of a query over a 32-key block sit in one
 //   lane and its partner lane 32 away: the row max needs one cross-half exchange
 //   (v_permlane32_swap) and the row sum none until the end;
-// * key/value tiles of 64 keys are staged through LDS with raw buffer loads whose
-//   hardware range check zero-fills rows past the sequence end. K and V are stored
-//   row-major; P.V reads its V^T operands with the transposing LDS read
-//   ds_read_b64_tr_b16. Row paddings (272-byte K rows, 320-byte V rows) keep every LDS
-//   read and write free of bank conflicts on the 64-bank LDS;
+// * key/value tiles of 64 keys go through LDS, fetched with raw buffer loads whose hardware
+//   range check zero-fills rows past the sequence end. K and V are stored row-major; P.V
+//   reads its V^T operands with the transposing LDS read ds_read_b64_tr_b16. bf16 tiles at
+//   head dimension 128 are loaded straight into LDS, unpadded, with 16-byte chunks XOR-
+//   swizzled per row; the other cases (head dimension 64, fp8) are staged through registers
+//   into padded rows (272-byte K rows, 320-byte V rows). Both layouts keep every LDS read
+//   free of bank conflicts on the 64-bank LDS;
 // * the running max is raised only when a tile's max exceeds it by more than 2^8 (in the
 //   exp2 domain): probabilities then stay below 256 and the O rescale becomes rare. The
 //   result is the same function; only the reference point of the exponentials moves;
@@ -31,9 +33,10 @@
 //   the previous tile, then S of the current one) the other runs its softmax on the vector
 //   ALU. Each SIMD holds one wave of each group, so one wave's products and the other's
 //   softmax are issued side by side (they overlap only in part: each slows the other).
-//   Tiles cycle through three LDS buffers so loads run two tiles ahead;
+//   Tiles cycle through four LDS stages (loaded into LDS) or three (register-staged), so
+//   loads run two tiles ahead;
 // * sparse kernel: 4 waves and one 128-row block per workgroup (the list granularity),
-//   two workgroups per CU, each step in one go, workgroups in plain order;
+//   two workgroups per CU, each step in one go, two LDS stages, workgroups in plain order;
 // * the LSE is written in natural log, O as bf16.
 #include "fa_common.h"
 #include "fa_internal.h"
