@@ -651,9 +651,13 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_dma_kernel(Params 
                 softmax<D, false, CAUSAL>(w, masked, kt, qrow, N, c, cpos, hf);
             }
         }
-        // After an odd phase the next one reads the step loaded two phase pairs ago: wait
-        // until only the latest step's four loads of this wave may still be in flight.
-        if (ph & 1) __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4), other counters unrestricted
+        // After odd phase 2m+1 the next phase reads step m+1: wait until only the loads of
+        // step m+2 (issued at the start of phase 2m, if there is such a step) may still be in
+        // flight, i.e. vmcnt(4), or until none are when step m+2 was not loaded.
+        if (ph & 1) {
+            if ((ph >> 1) + 2 < T) __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
+            else __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
+        }
         __syncthreads();
     }
     epilogue<D, false>(w, p.o + seq_off(sp, b, hh, p.osb, p.osh, p.osn), p.osn,
