@@ -55,6 +55,10 @@ FWD_CASES = [
     (1, 2, 300, 64, False, "bhnd", -0.2),
     (1, 1, 190, 128, True, "bhnd", 0.0),
     (1, 1, 257, 128, True, "bhnd", 0.9),
+    # six (sequence, head) pairs of short causal sequences: block-major order over groups
+    # of four pairs, the last group ragged
+    (3, 2, 1000, 128, True, "bnhd", None),
+    (3, 2, 777, 64, True, "bhnd", None),
 ]
 
 
