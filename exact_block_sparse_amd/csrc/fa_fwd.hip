@@ -291,14 +291,15 @@ __device__ __forceinline__ void softmax(Rows<D, F8>& w, bool masked, int kt0, in
 
     // The row sum is taken in fp32 over the unrounded probabilities (the LSE needs it);
     // P is rounded to bf16 only as the MFMA operand.
-    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four partial sums: short dependency chains
+    float ps[4];   // four partial sums (short dependency chains), each started by its first term
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const float pr = fast_exp2(fmaf(w.s[kb][r], ce, -m_use));
             w.s[kb][r] = pr;
-            ps[r & 3] += pr;
+            if (kb == 0 && r < 4) ps[r] = pr;
+            else ps[r & 3] += pr;
         }
     w.l_part += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
