@@ -195,9 +195,26 @@ struct Rows {
     QFrag<D, F8> qf;        // Q rows as B operands
     f32x16 o[C::CB];        // O^T accumulators
     float m_run, l_part;    // running max (exp2 domain) and this lane's partial row sum
+    float m_neg;            // -m_run, or 0 while m_run is -inf (the exponent's offset)
+    float m_thr;            // m_run + the rescale slack: a tile max above it raises m_run
     f32x16 s[2];            // scores of the current 64-key step (two 32-key blocks)
     bf16x8 pb[2][2];        // probabilities of the current step as bf16 B operands
 };
+
+// The kernels score with a non-negative scale: for a negative one they flip the sign of
+// their Q fragments (exact in bf16 and e4m3: the sign bit alone) and use its magnitude, so
+// the scores come out exactly negated and score x |scale| is bit for bit score x scale.
+// Then the largest scaled score of a tile is always its largest raw score, scaled.
+template <int D, bool F8>
+__device__ __forceinline__ float signed_scale(Rows<D, F8>& w, float c) {
+    if (c >= 0.0f) return c;
+#pragma unroll
+    for (int j = 0; j < (int)(sizeof(w.qf.v) / sizeof(w.qf.v[0])); ++j) {
+        if constexpr (F8) w.qf.v[j] ^= (int)0x80808080u;
+        else w.qf.v[j] = as_bf16x8(__builtin_bit_cast(u32x4, w.qf.v[j]) ^ 0x80008000u);
+    }
+    return -c;
+}
 
 // S^T = K Q^T for one 64-key step. Row i of each 32-key block; the two blocks' chains alternate.
 template <int D, bool F8>
@@ -239,7 +256,7 @@ __device__ __forceinline__ void scores(const uint16_t* buf, Rows<D, F8>& w, int 
 // Online softmax update for one step: mask (diagonal or tail tiles only), tile max, lazy
 // rescale, probabilities, fp32 row sum, bf16 operands. `masked` is uniform across the wave.
 template <int D, bool F8, bool CAUSAL>
-__device__ __forceinline__ void softmax(Rows<D, F8>& w, bool masked, int kt0, int qrow, int N, float c, bool cpos,
+__device__ __forceinline__ void softmax(Rows<D, F8>& w, bool masked, int kt0, int qrow, int N, float c,
                                         int hf) {
     using C = Cfg<D, F8>;
     // In masked tiles the scores are scaled here and masked keys (past the sequence end,
@@ -257,37 +274,31 @@ __device__ __forceinline__ void softmax(Rows<D, F8>& w, bool masked, int kt0, in
             }
         ce = 1.0f;
     }
-    float mt;
-    if (masked || cpos) {
-        mt = fmaxf(w.s[0][0], w.s[1][0]);
+    // Tile max of the scaled scores: the scale is never negative here (the kernels flip
+    // the sign of Q instead), so it is the scaled max of the raw scores. The NaN-propagating
+    // maximum needs no quieting of its inputs.
+    float mt = __builtin_elementwise_maximum(w.s[0][0], w.s[1][0]);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 1; r < 16; ++r) mt = fmaxf(mt, w.s[kb][r]);
-        mt = pair_max(mt);
-    } else {   // negative scale: the largest scaled score comes from the smallest raw one
-        mt = fminf(w.s[0][0], w.s[1][0]);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mt = fminf(mt, w.s[kb][r]);
-        mt = pair_min(mt);
-    }
+        for (int r = 1; r < 16; ++r) mt = __builtin_elementwise_maximum(mt, w.s[kb][r]);
+    mt = pair_max(mt);
     mt *= ce;
 
     // Raise the running max only when the tile would push a probability above 2^8.
-    const bool need = mt > w.m_run + kRescaleSlack;
+    const bool need = mt > w.m_thr;
     if (__any(need)) {
         const float m_new = need ? mt : w.m_run;
         const float alpha = need ? fast_exp2(w.m_run - m_new) : 1.0f;
         w.m_run = m_new;
+        w.m_neg = (m_new == kNegInf) ? 0.0f : -m_new;
+        w.m_thr = m_new + kRescaleSlack;
         w.l_part *= alpha;
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) w.o[cb][r] *= alpha;
     }
-    const float m_use = (w.m_run == kNegInf) ? 0.0f : w.m_run;
 
     // The row sum is taken in fp32 over the unrounded probabilities (the LSE needs it);
     // P is rounded to bf16 only as the MFMA operand.
@@ -296,7 +307,7 @@ __device__ __forceinline__ void softmax(Rows<D, F8>& w, bool masked, int kt0, in
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float pr = fast_exp2(fmaf(w.s[kb][r], ce, -m_use));
+            const float pr = fast_exp2(fmaf(w.s[kb][r], ce, w.m_neg));
             w.s[kb][r] = pr;
             if (kb == 0 && r < 4) ps[r] = pr;
             else ps[r & 3] += pr;
@@ -371,6 +382,8 @@ __device__ __forceinline__ void load_q(Rows<D, F8>& w, const typename ElemOf<F8>
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb) w.o[cb] = f32x16{};
     w.m_run = kNegInf;
+    w.m_neg = 0.0f;
+    w.m_thr = kNegInf;
     w.l_part = 0.0f;
 }
 
@@ -459,8 +472,6 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_kernel(Params p) {
     // key is not past the wave's last row.
     const int Tw = CAUSAL ? min(T, (qw0 + 31) / kBK + 1) : T;
     const bool rows_valid = qw0 < N;
-    const float c = p.c;
-    const bool cpos = c >= 0.0f;
 
     typename StageOf<D, kPPThreads, F8>::type st;
     st.init(tid, p.ksn, p.vsn);
@@ -471,6 +482,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_kernel(Params p) {
     // Settle every outstanding load (the Q fragments included) so that no wait on them is
     // left inside the loop; then start the loads of step 1.
     __builtin_amdgcn_s_waitcnt(0);
+    const float c = signed_scale(w, p.c);   // after the wait: Q is in registers
     if (T > 1) st.load(kp, vp, p.ksn, p.vsn, kBK, N);
     __syncthreads();
 
@@ -497,7 +509,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_kernel(Params p) {
             } else if (t < Tw) {
                 const int kt = t * kBK;
                 const bool masked = (kt + kBK > N) || (CAUSAL && kt + kBK - 1 > qw0);
-                softmax<D, F8, CAUSAL>(w, masked, kt, qrow, N, c, cpos, hf);
+                softmax<D, F8, CAUSAL>(w, masked, kt, qrow, N, c, hf);
             }
         }
         __syncthreads();
@@ -632,8 +644,6 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_dma_kernel(Params 
     if (CAUSAL) T = min(T, qlast / kBK + 1);
     const int Tw = CAUSAL ? min(T, (qw0 + 31) / kBK + 1) : T;
     const bool rows_valid = qw0 < N;
-    const float c = p.c;
-    const bool cpos = c >= 0.0f;
 
     DmaStage<kPPThreads / 64, kSwzRow, kSwzTr> st;
     st.init(wave, lane, p.ksn, p.vsn);
@@ -647,6 +657,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_dma_kernel(Params 
     if (T > 1) st.issue(kp, vp, p.ksn, p.vsn, kBK, N, lds0 + kDmaStageB, wave_u);
     // Settle every outstanding load (Q fragments and the first two steps) before the loop.
     __builtin_amdgcn_s_waitcnt(0);
+    const float c = signed_scale(w, p.c);   // after the wait: Q is in registers
     __syncthreads();
 
     // Phase ph: group g works on local phase lp = ph - g. Even lp = 2t: P.V of step t-1 and
@@ -667,7 +678,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_dma_kernel(Params 
             } else if (t < Tw) {
                 const int kt = t * kBK;
                 const bool masked = (kt + kBK > N) || (CAUSAL && kt + kBK - 1 > qw0);
-                softmax<D, false, CAUSAL>(w, masked, kt, qrow, N, c, cpos, hf);
+                softmax<D, false, CAUSAL>(w, masked, kt, qrow, N, c, hf);
             }
         }
         // After odd phase 2m+1 the next phase reads step m+1: wait until only the loads of
@@ -736,8 +747,6 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
     int kt = -1;
     while (t < t_end && (kt = step_key(t)) < 0) ++t;
 
-    const float c = p.c;
-    const bool cpos = c >= 0.0f;
 
     typename StageOf<D, kSpThreads, F8>::type st;
     st.init(tid, p.ksn, p.vsn);
@@ -748,6 +757,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
     // Settle every outstanding load (the Q fragments included) before the loop, so that no
     // wait on them is left inside it.
     __builtin_amdgcn_s_waitcnt(0);
+    const float c = signed_scale(w, p.c);   // after the wait: Q is in registers
     __syncthreads();
 
     int cur = 0;
@@ -765,7 +775,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
             __builtin_amdgcn_s_setprio(1);
             scores<D, F8>(buf, w, i, hf);
             __builtin_amdgcn_s_setprio(0);
-            softmax<D, F8, CAUSAL>(w, masked, kt, qrow, N, c, cpos, hf);
+            softmax<D, F8, CAUSAL>(w, masked, kt, qrow, N, c, hf);
             __builtin_amdgcn_s_setprio(1);
             pv<D, F8>(buf, w, i, hf);
             __builtin_amdgcn_s_setprio(0);
@@ -829,8 +839,6 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_dma_kernel(Params p)
     int kt = -1;
     while (t < t_end && (kt = step_key(t)) < 0) ++t;
 
-    const float c = p.c;
-    const bool cpos = c >= 0.0f;
 
     DmaStage<kSpThreads / 64, kSwzRow, kSwzTr> st;
     st.init(wave, lane, p.ksn, p.vsn);
@@ -840,6 +848,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_dma_kernel(Params p)
     const uint32_t lds0 = lds_address(smem);
     if (t < t_end) st.issue(kp, vp, p.ksn, p.vsn, kt, N, lds0, wave_u);
     __builtin_amdgcn_s_waitcnt(0);
+    const float c = signed_scale(w, p.c);   // after the wait: Q is in registers
     __syncthreads();
 
     int cur = 0;
@@ -856,7 +865,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_dma_kernel(Params p)
             __builtin_amdgcn_s_setprio(1);
             scores_sw(buf, w, ad);
             __builtin_amdgcn_s_setprio(0);
-            softmax<D, false, CAUSAL>(w, masked, kt, qrow, N, c, cpos, hf);
+            softmax<D, false, CAUSAL>(w, masked, kt, qrow, N, c, hf);
             __builtin_amdgcn_s_setprio(1);
             pv_sw(buf, w, ad);
             __builtin_amdgcn_s_setprio(0);

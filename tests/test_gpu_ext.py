@@ -471,6 +471,26 @@ def test_fp8_sparse_and_packed(fa):
     assert_close("LSE", lse, L, TOL_LSE)
 
 
+@pytest.mark.parametrize("sparse", [False, True])
+def test_fp8_negative_scale(fa, sparse):
+    # the e4m3 Q codes get their sign bit flipped and the scale's magnitude is used
+    w = W.small(1, 2, 300, 128, causal=True, seed=32, dtype="fp8_e4m3")
+    x = W.make_inputs(w)
+    g = {n: x[n].to("cuda") for n in "qkv"}
+    sc = float(np.float32(-1.3 * w.scale))
+    kw = {}
+    sp = None
+    if sparse:
+        off, idx, sp = lists_for((300 + 127) // 128, 1, 2, True)
+        kw = dict(kv_offsets=off, kv_indices=idx)
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], causal=True, scale=sc, **kw, **fp8_kw(x))
+    torch.cuda.synchronize()
+    O, L = oracle.attention_forward(dequant(x, "q"), dequant(x, "k"), dequant(x, "v"), causal=True, scale=sc,
+                                    sparse=sp)
+    assert_close("O", o, O, TOL_OUT)
+    assert_close("LSE", lse, L, TOL_LSE)
+
+
 def test_fp8_descales_scale_the_result(fa):
     # the same codes with V's descale doubled give exactly twice the output (a power of two);
     # doubling Q's descale and halving K's leaves the scores, so O and LSE are unchanged

@@ -181,6 +181,30 @@ def test_sparse_small(fa, B, H, N, d, causal, window, stride, rule):
         assert_close("O(dense)", o, f64(o2), TOL_OUT)
 
 
+# A negative scale: the kernels score -Q against K with the scale's magnitude (a sign flip
+# of the Q fragments), so the largest scaled score of a tile is always a tile max. Every
+# forward kernel: dense and block-sparse, head dimension 64 and 128, causal or not.
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_negative_scale_dense_and_sparse(fa, d, causal):
+    B, H, N = 1, 2, 128 * 3 + 45
+    sc = float(np.float32(-1.7 / np.sqrt(d)))
+    x = small_inputs(B, H, N, d, seed=77 + d)
+    q, k, v = (to_dev(x[n]) for n in "qkv")
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=sc)
+    nb = (N + 127) // 128
+    off, idx = fa.make_block_lists(nb, 1, 2, causal=causal, rule="strided")
+    o_s, lse_s = fa.sparse_fwd(q, k, v, off, idx, causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention_forward(x["q"], x["k"], x["v"], causal=causal, scale=sc)
+    assert_close("O", o, O_ref, TOL_OUT)
+    assert_close("LSE", lse, L_ref, TOL_LSE)
+    sp = dict(block=128, window=1, stride=2, rule="strided")
+    O_sp, L_sp = oracle.attention_forward(x["q"], x["k"], x["v"], causal=causal, scale=sc, sparse=sp)
+    assert_close("O(sparse)", o_s, O_sp, TOL_OUT)
+    assert_close("LSE(sparse)", lse_s, L_sp, TOL_LSE)
+
+
 def test_sparse_hand_lists_with_empty_block(fa):
     N, d = 128 * 5, 128
     x = small_inputs(1, 1, N, d, seed=3)
