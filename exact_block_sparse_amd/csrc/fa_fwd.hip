@@ -194,7 +194,8 @@ struct Rows {
     using C = Cfg<D, F8>;
     QFrag<D, F8> qf;        // Q rows as B operands
     f32x16 o[C::CB];        // O^T accumulators
-    float m_run, l_part;    // running max (exp2 domain) and this lane's partial row sum
+    float m_run;            // running max (exp2 domain)
+    float l4[4];            // this lane's row sum in four interleaved parts (short add chains)
     float m_neg;            // -m_run, or 0 while m_run is -inf (the exponent's offset)
     float m_thr;            // m_run + the rescale slack: a tile max above it raises m_run
     f32x16 s[2];            // scores of the current 64-key step (two 32-key blocks)
@@ -293,7 +294,8 @@ __device__ __forceinline__ void softmax(Rows<D, F8>& w, bool masked, int kt0, in
         w.m_run = m_new;
         w.m_neg = (m_new == kNegInf) ? 0.0f : -m_new;
         w.m_thr = m_new + kRescaleSlack;
-        w.l_part *= alpha;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w.l4[j] *= alpha;
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
@@ -302,17 +304,14 @@ __device__ __forceinline__ void softmax(Rows<D, F8>& w, bool masked, int kt0, in
 
     // The row sum is taken in fp32 over the unrounded probabilities (the LSE needs it);
     // P is rounded to bf16 only as the MFMA operand.
-    float ps[4];   // four partial sums (short dependency chains), each started by its first term
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const float pr = fast_exp2(fmaf(w.s[kb][r], ce, w.m_neg));
             w.s[kb][r] = pr;
-            if (kb == 0 && r < 4) ps[r] = pr;
-            else ps[r & 3] += pr;
+            w.l4[r & 3] += pr;
         }
-    w.l_part += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -384,7 +383,8 @@ __device__ __forceinline__ void load_q(Rows<D, F8>& w, const typename ElemOf<F8>
     w.m_run = kNegInf;
     w.m_neg = 0.0f;
     w.m_thr = kNegInf;
-    w.l_part = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w.l4[j] = 0.0f;
 }
 
 // O = O^T / l as bf16; LSE = (m + log2 l) * ln 2. `obase` and `lbase` point at row 0 of the
@@ -393,7 +393,7 @@ template <int D, bool F8>
 __device__ __forceinline__ void epilogue(const Rows<D, F8>& w, uint16_t* obase, int64_t osn, float* lbase, int qrow,
                                          int N, int hf, float vdesc) {
     using C = Cfg<D, F8>;
-    const float l_tot = pair_sum(w.l_part);
+    const float l_tot = pair_sum((w.l4[0] + w.l4[1]) + (w.l4[2] + w.l4[3]));
     if (qrow >= N) return;
     const float inv = l_tot > 0.0f ? vdesc / l_tot : 0.0f;
     uint16_t* orow = obase + (int64_t)qrow * osn;
@@ -539,37 +539,52 @@ constexpr int kDmaRowB = kLdsRowB;
 constexpr int kDmaTileB = kLdsTileB;
 constexpr int kDmaStageB = 2 * kDmaTileB;        // K then V
 
-// Per-lane byte offsets (within a stage) of the swizzled reads.
+// Per-lane LDS byte addresses of the swizzled reads in stage 0 (the LDS base of the stages
+// included, so that a read's address is one add of the stage offset).
 struct DmaAddr {
     uint32_t k[8];   // K: row i, logical chunk 2 * ks + hf (the second 32-key block is +8 KB)
     uint32_t v[4];   // V (transposing reads): per 32-column block cb
 
-    __device__ void init(int i, int hf) {
+    __device__ void init(int i, int hf, uint32_t base) {
+        // Hide the base's value (0 for the kernels' single LDS array) from the compiler:
+        // known-disjoint address bits make it combine the stage and block offsets with ORs
+        // instead of one add plus the read's immediate offset.
+        asm("" : "+s"(base));
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) k[ks] = (uint32_t)(i * kDmaRowB + 16 * ((2 * ks + hf) ^ swz<kSwzRow>(i)));
+        for (int ks = 0; ks < 8; ++ks)
+            k[ks] = base + (uint32_t)(i * kDmaRowB + 16 * ((2 * ks + hf) ^ swz<kSwzRow>(i)));
         const int g16 = (i >> 4) & 1, j16 = i & 15;
         const int row = 4 * hf + (j16 >> 2);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             const int chunk = 4 * cb + 2 * g16 + ((j16 & 3) >> 1);
-            v[cb] = (uint32_t)(kDmaTileB + row * kDmaRowB + 16 * (chunk ^ swz<kSwzTr>(row)) + 8 * (j16 & 1));
+            v[cb] = base + (uint32_t)(kDmaTileB + row * kDmaRowB + 16 * (chunk ^ swz<kSwzTr>(row)) + 8 * (j16 & 1));
         }
     }
 };
 
-__device__ __forceinline__ const bf16x8& lds16(const unsigned char* base, uint32_t off) {
-    return *reinterpret_cast<const bf16x8*>(base + off);
+// 16-byte row read and 8-byte transposing read at an LDS byte address.
+__device__ __forceinline__ bf16x8 lds16(uint32_t addr) {
+    return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)addr;
+}
+__device__ __forceinline__ u32x2 lds_tr4(uint32_t addr) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)addr));
 }
 
-// S^T = K Q^T for one 64-key step from a swizzled stage (same products as scores()).
-__device__ __forceinline__ void scores_sw(const unsigned char* st, Rows<128, false>& w, const DmaAddr& a) {
+// S^T = K Q^T for one 64-key step from the swizzled stage at byte offset `so` (same products
+// as scores()).
+__device__ __forceinline__ void scores_sw(uint32_t so, Rows<128, false>& w, const DmaAddr& a) {
     w.s[0] = f32x16{};
     w.s[1] = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+    for (int ks = 0; ks < 8; ++ks) {
+        uint32_t x = a.k[ks] + so;
+        asm("" : "+v"(x));   // one add per column; the block offset goes to the read's immediate
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-            w.s[kb] = mfma32(lds16(st, a.k[ks] + 32 * kDmaRowB * kb), w.qf.v[ks], w.s[kb]);
+        for (int kb = 0; kb < 2; ++kb) w.s[kb] = mfma32(lds16(x + 32 * kDmaRowB * kb), w.qf.v[ks], w.s[kb]);
+    }
     constexpr int N = 16, AHEAD = 6;
     __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
 #pragma unroll
@@ -580,18 +595,21 @@ __device__ __forceinline__ void scores_sw(const unsigned char* st, Rows<128, fal
     __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 }
 
-// O^T += V^T P^T from a swizzled stage (same products and operand layout as pv()).
-__device__ __forceinline__ void pv_sw(const unsigned char* st, Rows<128, false>& w, const DmaAddr& a) {
+// O^T += V^T P^T from the swizzled stage at byte offset `so` (same products and operand
+// layout as pv()).
+__device__ __forceinline__ void pv_sw(uint32_t so, Rows<128, false>& w, const DmaAddr& a) {
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
         bf16x8 op[2][2];
+        uint32_t xv = a.v[cb] + so;
+        asm("" : "+v"(xv));   // one add per column block; row offsets go to the immediates
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                const unsigned char* p0 = st + a.v[cb] + (32 * kb + 16 * s2) * kDmaRowB;
-                const u32x2 lo = lds_read_tr4(reinterpret_cast<const uint16_t*>(p0));
-                const u32x2 hi = lds_read_tr4(reinterpret_cast<const uint16_t*>(p0 + 8 * kDmaRowB));
+                const uint32_t p0 = xv + (32 * kb + 16 * s2) * kDmaRowB;
+                const u32x2 lo = lds_tr4(p0);
+                const u32x2 hi = lds_tr4(p0 + 8 * kDmaRowB);
                 u32x4 x;
                 x[0] = lo[0]; x[1] = lo[1]; x[2] = hi[0]; x[3] = hi[1];
                 op[kb][s2] = as_bf16x8(x);
@@ -648,7 +666,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_dma_kernel(Params 
     DmaStage<kPPThreads / 64, kSwzRow, kSwzTr> st;
     st.init(wave, lane, p.ksn, p.vsn);
     DmaAddr ad;
-    ad.init(i, hf);
+    ad.init(i, hf, lds_address(smem));
     // the wave index and the LDS base are uniform: keep them in scalar registers (the loads
     // take their LDS address from M0)
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -672,8 +690,8 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_dma_kernel(Params 
             const int t = lp >> 1;
             if ((lp & 1) == 0) {
                 __builtin_amdgcn_s_setprio(1);
-                if (t >= 1 && t - 1 < Tw) pv_sw(smem + ((t - 1) % kDmaBufs) * kDmaStageB, w, ad);
-                if (t < Tw) scores_sw(smem + (t % kDmaBufs) * kDmaStageB, w, ad);
+                if (t >= 1 && t - 1 < Tw) pv_sw(((t - 1) % kDmaBufs) * kDmaStageB, w, ad);
+                if (t < Tw) scores_sw((t % kDmaBufs) * kDmaStageB, w, ad);
                 __builtin_amdgcn_s_setprio(0);
             } else if (t < Tw) {
                 const int kt = t * kBK;
@@ -843,7 +861,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_dma_kernel(Params p)
     DmaStage<kSpThreads / 64, kSwzRow, kSwzTr> st;
     st.init(wave, lane, p.ksn, p.vsn);
     DmaAddr ad;
-    ad.init(i, hf);
+    ad.init(i, hf, lds_address(smem));
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t lds0 = lds_address(smem);
     if (t < t_end) st.issue(kp, vp, p.ksn, p.vsn, kt, N, lds0, wave_u);
@@ -859,7 +877,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_dma_kernel(Params p)
         // the other stage was last read in the previous step, which ended with a barrier
         if (has_next) st.issue(kp, vp, p.ksn, p.vsn, ktn, N, lds0 + (cur ^ 1) * kDmaStageB, wave_u);
 
-        const unsigned char* buf = smem + cur * kDmaStageB;
+        const uint32_t buf = cur * kDmaStageB;
         if (qw0 < N && (!CAUSAL || kt <= qw0 + 31)) {
             const bool masked = (kt + kBK > N) || (CAUSAL && kt + kBK - 1 > qw0);
             __builtin_amdgcn_s_setprio(1);
