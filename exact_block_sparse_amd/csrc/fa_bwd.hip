@@ -580,16 +580,21 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(QParams p) {
                     sacc = mfma32(*reinterpret_cast<const bf16x8*>(kr + 16 * ks), qf[ks], sacc);
                     pacc = mfma32(*reinterpret_cast<const bf16x8*>(vr + 16 * ks), df[ks], pacc);
                 }
+                // P from the LSE; in diagonal and tail tiles the masked keys' probabilities
+                // are zeroed in one block the wave skips elsewhere (a test inside the element
+                // loop became an exec-masked region per element, executed on every tile).
                 float dsv[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float pe = fast_exp2(fmaf(sacc[r], c, -lse2));
-                    if (masked) {
+                for (int r = 0; r < 16; ++r) dsv[r] = fast_exp2(fmaf(sacc[r], c, -lse2));
+                if (masked) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
                         const int kk = kt + 32 * kb + acc_row(r, hf);
-                        if (kk >= N || (CAUSAL && kk > qrow)) pe = 0.0f;
+                        if (kk >= N || (CAUSAL && kk > qrow)) dsv[r] = 0.0f;
                     }
-                    dsv[r] = pe * (pacc[r] - dlt);
                 }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dsv[r] *= pacc[r] - dlt;
 #pragma unroll
                 for (int st = 0; st < 2; ++st)
                     db[kb][st] = pack8(dsv[8 * st], dsv[8 * st + 1], dsv[8 * st + 2], dsv[8 * st + 3],
@@ -754,16 +759,21 @@ __global__ __launch_bounds__(kThreads, 2) void dq_dma_kernel(QParams p) {
                     sacc = mfma32(*reinterpret_cast<const bf16x8*>(kr + ar[ks]), qf[ks], sacc);
                     pacc = mfma32(*reinterpret_cast<const bf16x8*>(kr + kLdsTileB + ar[ks]), df[ks], pacc);
                 }
+                // P from the LSE; in diagonal and tail tiles the masked keys' probabilities
+                // are zeroed in one block the wave skips elsewhere (a test inside the element
+                // loop became an exec-masked region per element, executed on every tile).
                 float dsv[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float pe = fast_exp2(fmaf(sacc[r], c, -lse2));
-                    if (masked) {
+                for (int r = 0; r < 16; ++r) dsv[r] = fast_exp2(fmaf(sacc[r], c, -lse2));
+                if (masked) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
                         const int kk = kt + 32 * kb + acc_row(r, hf);
-                        if (kk >= N || (CAUSAL && kk > qrow)) pe = 0.0f;
+                        if (kk >= N || (CAUSAL && kk > qrow)) dsv[r] = 0.0f;
                     }
-                    dsv[r] = pe * (pacc[r] - dlt);
                 }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dsv[r] *= pacc[r] - dlt;
 #pragma unroll
                 for (int st = 0; st < 2; ++st)
                     db[kb][st] = pack8(dsv[8 * st], dsv[8 * st + 1], dsv[8 * st + 2], dsv[8 * st + 3],
