@@ -587,11 +587,12 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(QParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) dsv[r] = fast_exp2(fmaf(sacc[r], c, -lse2));
                 if (masked) {
+                    // key of element r: kt + 4 hf + 32 kb + 8 (r / 4) + r % 4 (acc_row)
+                    int lim = N - 1 - kt - 4 * hf - 32 * kb;
+                    if (CAUSAL) lim = min(lim, qrow - kt - 4 * hf - 32 * kb);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int kk = kt + 32 * kb + acc_row(r, hf);
-                        if (kk >= N || (CAUSAL && kk > qrow)) dsv[r] = 0.0f;
-                    }
+                    for (int r = 0; r < 16; ++r)
+                        if (8 * (r >> 2) + (r & 3) > lim) dsv[r] = 0.0f;
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) dsv[r] *= pacc[r] - dlt;
@@ -766,11 +767,12 @@ __global__ __launch_bounds__(kThreads, 2) void dq_dma_kernel(QParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) dsv[r] = fast_exp2(fmaf(sacc[r], c, -lse2));
                 if (masked) {
+                    // key of element r: kt + 4 hf + 32 kb + 8 (r / 4) + r % 4 (acc_row)
+                    int lim = N - 1 - kt - 4 * hf - 32 * kb;
+                    if (CAUSAL) lim = min(lim, qrow - kt - 4 * hf - 32 * kb);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int kk = kt + 32 * kb + acc_row(r, hf);
-                        if (kk >= N || (CAUSAL && kk > qrow)) dsv[r] = 0.0f;
-                    }
+                    for (int r = 0; r < 16; ++r)
+                        if (8 * (r >> 2) + (r & 3) > lim) dsv[r] = 0.0f;
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) dsv[r] *= pacc[r] - dlt;

@@ -265,13 +265,17 @@ __device__ __forceinline__ void softmax(Rows<D, F8>& w, bool masked, int kt0, in
     // a unit multiplier. Elsewhere the scale is folded into the exponent's FMA.
     float ce = c;
     if (masked) {
+        // Element (kb, r) holds key kt0 + 4 hf + 32 kb + 8 (r / 4) + r % 4 (acc_row): one
+        // per-lane limit turns both tests (key < N, causal key <= qrow) into a single
+        // compare with a compile-time offset.
+        int lim = N - 1 - kt0 - 4 * hf;
+        if (CAUSAL) lim = min(lim, qrow - kt0 - 4 * hf);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key = kt0 + 32 * kb + acc_row(r, hf);
-                const bool ok = key < N && (!CAUSAL || key <= qrow);
-                w.s[kb][r] = ok ? w.s[kb][r] * c : kNegInf;
+                const int rel = 32 * kb + 8 * (r >> 2) + (r & 3);
+                w.s[kb][r] = rel <= lim ? w.s[kb][r] * c : kNegInf;
             }
         ce = 1.0f;
     }
