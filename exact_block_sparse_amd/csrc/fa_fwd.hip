@@ -917,11 +917,14 @@ hipError_t dispatch(Params p, bool sparse, hipStream_t stream) {
     p.nqb = (p.N + kPPRows - 1) / kPPRows;
     const int64_t grid = (int64_t)p.B * p.H * p.nqb;
     // Short causal sequences (at most 16 query blocks per head): block-major order over
-    // groups of four (head, sequence) pairs, so that an XCD's share does not end on the
-    // longest blocks of its last pairs (B=4 H=32 N=4096: +5 %). Longer sequences keep plain
-    // head-major order: their shares already balance, and groups lose L2 reuse of the K/V
-    // stream (N=32768: -4 % with groups of four); packed batches lost 15-30 % with any group.
-    p.gh = (CAUSAL && p.cu == nullptr && p.nqb <= 16) ? 4 : 1;
+    // groups of (head, sequence) pairs, so that an XCD's share does not end on the longest
+    // blocks of its last pairs. A group holds at most the pairs of one XCD's share (B*H/8)
+    // and at most eight (B=4 H=32 N=4096: groups of 4 +5 %, of 8 +9 %, of 16 +7 % over
+    // plain order). Longer sequences keep plain head-major order: their shares already
+    // balance, and groups lose L2 reuse of the K/V stream (N=32768: -4 % with groups of
+    // four, -40 % with groups wider than a share); packed batches lost 15-30 % with any group.
+    p.gh = 1;
+    if (CAUSAL && p.cu == nullptr && p.nqb <= 16) p.gh = max(1, min(8, p.B * p.H / 8));
     if constexpr (D == 128 && !F8)
         hipLaunchKernelGGL((fwd_pingpong_dma_kernel<CAUSAL>), dim3((unsigned)grid), dim3(kPPThreads), 0, stream, p);
     else

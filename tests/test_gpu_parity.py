@@ -55,8 +55,7 @@ FWD_CASES = [
     (1, 2, 300, 64, False, "bhnd", -0.2),
     (1, 1, 190, 128, True, "bhnd", 0.0),
     (1, 1, 257, 128, True, "bhnd", 0.9),
-    # six (sequence, head) pairs of short causal sequences: block-major order over groups
-    # of four pairs, the last group ragged
+    # six (sequence, head) pairs of short causal sequences
     (3, 2, 1000, 128, True, "bnhd", None),
     (3, 2, 777, 64, True, "bhnd", None),
 ]
@@ -84,6 +83,7 @@ PERSISTENT_CASES = [
     (1, 33, 2048, True, "bhnd"),
     (3, 11, 2100, False, "bnhd"),
     (2, 40, 1800, True, "bnhd"),
+    (3, 22, 1000, True, "bnhd"),   # 66 pairs of short causal sequences: groups of 8, the last ragged
 ]
 
 
