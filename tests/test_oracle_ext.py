@@ -284,3 +284,79 @@ def test_fp8_dequantisation_is_exact_in_fp64():
     deq = q * x["q_descale"]
     assert np.array_equal(deq / x["q_descale"], q)
     assert np.abs(q).max() <= 448.0
+
+
+# ----------------------------------------------------------------------------- sampled query gradients
+def _masked_autograd_dq(Q, K, V, dO, scale, mask, G):
+    """dQ by torch fp64 autograd of softmax(scale Q K^T + mask) V with K, V replicated over
+    groups of G query heads. Rows without any allowed key have P = 0 (and so dQ = 0): their
+    scores are replaced by zeros and their probabilities multiplied by 0, which keeps the
+    graph free of NaN."""
+    q = Q.clone().requires_grad_(True)
+    k = K.repeat_interleave(G, dim=1)
+    v = V.repeat_interleave(G, dim=1)
+    has = mask.any(-1, keepdim=True)
+    S = (scale * q @ k.transpose(-1, -2)).masked_fill(~mask, -math.inf)
+    S = torch.where(has, S, torch.zeros_like(S))
+    P = torch.softmax(S, -1) * has
+    (P @ v).backward(dO)
+    return q.grad
+
+
+@pytest.mark.parametrize("kind", ["dense", "causal", "lists", "rule"])
+def test_sampled_query_gradients_match_autograd(kind):
+    """backward_rows_dq (the dQ reference at sizes where the whole backward is too slow)
+    against torch fp64 autograd, at a batch and query head other than (0, 0) of a grouped
+    problem (H = 6 over H_kv = 2), for dense, causal and block-sparse masks; the explicit
+    lists give one query block an empty list (its rows: dQ = 0) and one an entry above the
+    diagonal (skipped under causal masking)."""
+    from oracle import backward_rows_dq, block_lists as bl
+    g = torch.Generator().manual_seed(53)
+    B, H, H_kv, n, d, blk = 2, 6, 2, 43, 8, 8
+    G = H // H_kv
+    Q, dO = t64((B, H, n, d), g), t64((B, H, n, d), g)
+    K, V = t64((B, H_kv, n, d), g), t64((B, H_kv, n, d), g)
+    causal = kind != "dense"
+    mask = torch.tril(torch.ones(n, n, dtype=torch.bool)) if causal else torch.ones(n, n, dtype=torch.bool)
+    sparse = None
+    nb = (n + blk - 1) // blk
+    if kind == "lists":
+        # block 2 lists nothing; block 3 lists block 4 (above it: skipped) besides 1 and 3
+        lists = {0: [0], 1: [0, 1], 2: [], 3: [1, 3, 4], 4: [2, 4], 5: [0, 5]}
+        off = np.cumsum([0] + [len(lists[q]) for q in range(nb)]).astype(np.int64)
+        idx = np.array([k for q in range(nb) for k in lists[q]], dtype=np.int64)
+        sparse = dict(block=blk, offsets=off, indices=idx)
+        mask &= torch.from_numpy(key_mask_from_lists(n, blk, off, idx, True))
+        assert not mask[2 * blk:3 * blk].any()
+    elif kind == "rule":
+        off, idx = bl(nb, 1, 3, True, "strided")
+        sparse = dict(block=blk, window=1, stride=3, rule="strided")
+        mask &= torch.from_numpy(key_mask_from_lists(n, blk, off, idx, True))
+    want = _masked_autograd_dq(Q, K, V, dO, 0.37, mask, G)
+    rows = [0, 1, 7, 8, 16, 17, 23, 25, 31, 40, 42]
+    for b, h in ((1, 4), (0, 5), (1, 2)):
+        got = backward_rows_dq(Q.numpy(), K.numpy(), V.numpy(), dO.numpy(), causal=causal, scale=0.37,
+                               sparse=sparse, b=b, h=h, rows=rows)
+        assert sorted(got) == rows
+        for i in rows:
+            np.testing.assert_allclose(got[i], want[b, h, i].numpy(), atol=1e-12, rtol=0)
+    if kind == "lists":
+        got = backward_rows_dq(Q.numpy(), K.numpy(), V.numpy(), dO.numpy(), causal=True, scale=0.37,
+                               sparse=sparse, b=1, h=4, rows=range(2 * blk, 3 * blk))
+        assert all(np.all(got[i] == 0) for i in range(2 * blk, 3 * blk))
+
+
+def test_sampled_query_gradients_agree_with_the_full_backward():
+    """Same rows from backward_rows_dq and from attention_backward (grouped, causal, block
+    rule): a mistake in either one's head mapping, scale or D fails here or above."""
+    from oracle import backward_rows_dq
+    g = torch.Generator().manual_seed(54)
+    B, H, H_kv, n, d = 1, 4, 1, 37, 8
+    Q, dO = t64((B, H, n, d), g), t64((B, H, n, d), g)
+    K, V = t64((B, H_kv, n, d), g), t64((B, H_kv, n, d), g)
+    sp = dict(block=8, window=1, stride=2, rule="strided")
+    dQ, _, _ = attention_backward(Q.numpy(), K.numpy(), V.numpy(), dO.numpy(), causal=True, scale=0.5, sparse=sp)
+    for h in range(H):
+        got = backward_rows_dq(Q.numpy(), K.numpy(), V.numpy(), dO.numpy(), causal=True, scale=0.5, sparse=sp,
+                               h=h, rows=range(n))
+        np.testing.assert_allclose(np.stack([got[i] for i in range(n)]), dQ[0, h], atol=1e-12, rtol=0)
