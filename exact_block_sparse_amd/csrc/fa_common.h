@@ -244,11 +244,17 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
 // 16 bytes per lane from the buffer at byte offset `voff` into LDS at `lds` + 16 * lane
 // (`lds` wave-uniform). No register receives data, so nothing is left for the compiler to
 // reuse while the load is in flight.
+// The block sets M0 itself and the load reads it at once. M0 is a register the compiler
+// reserves: it does not honour it in a clobber list (so none is given), and the block is
+// correct only because nothing the compiler emits in these kernels keeps a value in M0
+// across it. The library build checks that on the generated assembly: every M0 reference
+// and every load into LDS must sit inside one of these blocks, and nothing else may use
+// M0 implicitly (relative register moves, messages, GWS or ordered-count operations).
 __device__ __forceinline__ void load16_to_lds(i32x4 r, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
                  : "v"(voff), "s"(r), "s"(lds)
-                 : "memory", "m0");
+                 : "memory");
 }
 
 // Per-thread part of one step's K and V loads: a 64-row tile is 16 pieces of 1 KB; each of
