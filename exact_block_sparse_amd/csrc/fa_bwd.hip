@@ -172,7 +172,6 @@ __device__ __forceinline__ f32x4v mfma16(bf16x8 a, bf16x8 b, f32x4v c) {
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
-    using C = BCfg<D>;
     using L = KVCfg<D>;
     constexpr int KS32 = D / 32;   // 32-wide k-steps over the head dimension
     constexpr int CB16 = D / 16;   // 16-row blocks of dK^T, dV^T
@@ -217,11 +216,12 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
     // turn. Dense: the tiles from the first one that can see these keys (causal) or from 0 to
     // the end. Block-sparse: both halves of every query block the key-side list names for
     // this key block. Under causal masking only the steps of the diagonal block hold keys
-    // after queries: the first two of each query head (dense), or the two halves of the list's
-    // first entry when it is the diagonal block (lists ascend); they are taken first, so the
-    // others run without the element test. Out-of-range list entries (or, causal, entries
-    // above the diagonal) become an empty tile at row N: zero-filled loads, LSE = +inf, so
-    // their probabilities are exactly 0.
+    // after queries: the first two of each query head (dense), or the two halves of the
+    // list's diagonal entry (block-sparse: the first entry not below the key block, the lists
+    // being ascending; entries before it are above-diagonal entries of the query-side lists,
+    // which are skipped). Those steps are taken first, so the others run without the element
+    // test. Out-of-range list entries (or, causal, entries above the diagonal) become an empty
+    // tile at row N: zero-filled loads, LSE = +inf, so their probabilities are exactly 0.
     const int nsteps = (N + kStep - 1) / kStep;
     const int t0 = CAUSAL ? k0 / kStep : 0;
     int64_t lo = 0, hi = 0;
@@ -235,7 +235,20 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
     const int per = sparse ? (int)(2 * (hi - lo)) : nsteps - t0;
     const int n_all = per * p.G;
     const int nqb = (N + kKV_BK - 1) / kKV_BK;
-    const int m_per = !CAUSAL ? 0 : (sparse ? ((hi > lo && load_uniform(p.q_indices, lo) == kblk) ? 2 : 0) : min(2, per));
+    int m_per = 0;      // masked steps per query head: 0, 2, or 1 when a head has a single step
+    int diag = 0;       // block-sparse: list position (from lo) of the diagonal entry
+    if constexpr (CAUSAL) {
+        if (sparse) {
+            int64_t e = lo;
+            while (e < hi && load_uniform(p.q_indices, e) < kblk) ++e;
+            if (e < hi && load_uniform(p.q_indices, e) == kblk) {
+                m_per = 2;
+                diag = (int)(e - lo);
+            }
+        } else {
+            m_per = min(2, per);
+        }
+    }
     const int n_mask = m_per * p.G;
     const int u_per = per - m_per;
     auto step_row = [&](int s, int& hq) -> int {   // first row of step s; N past the last step
@@ -243,18 +256,26 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
             hq = hk * p.G;
             return N;
         }
-        int gq, j;
-        if (s < n_mask) {
-            gq = s / m_per;
-            j = s - gq * m_per;
-        } else {
+        int gq = 0, j = 0;   // query head in the group; step within that head's sequence
+        bool masked_step = false;
+        if constexpr (CAUSAL) {
+            if (s < n_mask) {
+                gq = s / m_per;
+                j = s - gq * m_per;
+                masked_step = true;
+            }
+        }
+        if (!masked_step) {
             const int u = s - n_mask;
             gq = u / u_per;
-            j = m_per + (u - gq * u_per);
+            j = u - gq * u_per;   // among the unmasked steps
         }
         hq = hk * p.G + gq;
-        if (!sparse) return (t0 + j) * kStep;
-        const int qb = load_uniform(p.q_indices, lo + (j >> 1));
+        if (!sparse) return (t0 + (masked_step ? j : m_per + j)) * kStep;
+        int e = j >> 1;   // list entry (from lo): the diagonal one, or the others in order
+        if (masked_step) e = diag;
+        else if (m_per && e >= diag) ++e;
+        const int qb = load_uniform(p.q_indices, lo + e);
         if (qb < 0 || qb >= nqb || (CAUSAL && qb < kblk)) return N;
         const int r0 = qb * kKV_BK + (j & 1) * kStep;
         return r0 < N ? r0 : N;
