@@ -40,6 +40,19 @@ constexpr int64_t kMaxRowsFwd = (int64_t)1 << 30;
 constexpr int64_t kMaxRowsBwd = (int64_t)1 << 29;
 // Token stride in elements: the tile loaders address a 64-row tile with 32-bit byte offsets.
 constexpr int64_t kMaxRowStride = (int64_t)1 << 24;
+// Work-items of the largest launch of a call, from its grid (N: the longest sequence when
+// packed): forward, 512 threads per 256 query rows (dense) or 256 per 128 (block-sparse);
+// backward, 512 threads per 128 keys (dK, dV) and 256 per 128 query rows (dQ). Keeping it
+// at most 2^31 keeps the 32-bit grid size and the kernels' int workgroup indices from
+// wrapping; the row limits above alone do not (a batch of tiny sequences, or a packed
+// batch of many sequences with one long one, has far more workgroups than rows / 128).
+constexpr int64_t kMaxItems = (int64_t)1 << 31;
+int64_t launch_items(const fa_attn_desc& d, bool backward) {
+    const int64_t bh = d.B * d.H, u128 = (d.N + 127) / 128, u256 = (d.N + 255) / 256;
+    if (backward) return bh * u128 * 512;
+    const int64_t dense = bh * u256 * 512, sparse = bh * u128 * 256;
+    return dense > sparse ? dense : sparse;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -106,6 +119,10 @@ int check_desc(const fa_attn_desc* dp, bool backward) {
     const int64_t max_rows = backward ? kMaxRowsBwd : kMaxRowsFwd;
     if (rows > max_rows)
         return fail(FA_ERR_SHAPE, "%lld query rows in one call exceed %lld", (long long)rows, (long long)max_rows);
+    const int64_t items = launch_items(d, backward);
+    if (items > kMaxItems)
+        return fail(FA_ERR_SHAPE, "a launch would need %lld work-items, more than %lld (B=%lld H=%lld N=%lld)",
+                    (long long)items, (long long)kMaxItems, (long long)d.B, (long long)d.H, (long long)d.N);
     if (!std::isfinite(d.scale)) return fail(FA_ERR_ARG, "scale is not finite");
     if (d.dtype != FA_DTYPE_BF16 && d.dtype != FA_DTYPE_FP8_E4M3) return fail(FA_ERR_ARG, "unknown dtype %d", d.dtype);
     if (d.dtype == FA_DTYPE_FP8_E4M3) {

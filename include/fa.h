@@ -20,8 +20,12 @@
  * elements. LSE is fp32, contiguous [B, H, N], natural logarithm.
  *
  * Sizes (else FA_ERR_SHAPE): B, H, N (and H_kv, packed total) at most 2^30 each, B*H at
- * most 2^30, and at most 2^30 query rows (B*H*N, or H*total when packed) per forward call,
- * 2^29 per backward call; the kernels index workgroups and grids with 32-bit integers.
+ * most 2^30, at most 2^30 query rows (B*H*N, or H*total when packed) per forward call,
+ * 2^29 per backward call, and at most 2^31 work-items in any launch: forward
+ * B*H*ceil(N/256)*512 and B*H*ceil(N/128)*256, backward B*H*ceil(N/128)*512 (with packed
+ * sequences N is the longest sequence, so a batch of many sequences with one long one can
+ * hit this limit before the row limit); the kernels index workgroups and grids with 32-bit
+ * integers.
  *
  * Ownership and execution. The caller allocates and owns every buffer (device memory for
  * tensors, lists and workspace; host memory only where a parameter says "host"). The
@@ -171,8 +175,10 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, co
  * H_kv = H is plain multi-head attention, H_kv = 1 multi-query attention). dK and dV of a
  * K/V head are the sums over the query heads that read it.
  *
- * Packed variable-length sequences (same page, production notes on request batching: the
- * softmax of every tile ignores padding; and its FAQ on the varlen entry point). With
+ * Packed variable-length sequences (same page, section "The Production Pipeline: From
+ * Kernel to Service", on request batching: the softmax of every tile ignores padding; and
+ * "How to Use Flash MSA Kernels for Long Context", FAQ on flash-batch inference, which
+ * points to a variable-length entry point for sequences of different lengths). With
  * cu_seqlens != NULL the B sequences are packed one after another along the token axis of
  * [total, heads, d] tensors: sequence b is rows cu_seqlens[b] .. cu_seqlens[b+1]-1 and
  * attends only to itself (causal positions and block numbers count from its first row).
@@ -191,7 +197,10 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, co
  * With packed sequences the lists apply to every sequence, block numbers counted from the
  * sequence's first row; they must cover ceil(N / block_size) blocks.
  *
- * FP8 inputs (forward only; the page's FAQ on FP16 vs FP8 names FP8 attention). With
+ * FP8 inputs (forward only; "How to Use Flash MSA Kernels for Long Context", FAQ on FP16
+ * vs FP8, names FP8 attention; "Flash MSA Attention Kernel Implementation: A Practical
+ * Guide for Production AI", section "Optimization Tricks That Actually Matter", runs the
+ * tile's matrix products in FP8 and keeps the softmax in fp32). With
  * dtype = FA_DTYPE_FP8_E4M3, q, k and v hold OCP e4m3 codes (1 byte, strides in bytes,
  * multiples of 16) and each tensor's real values are code x descale (q_descale, k_descale,
  * v_descale; finite). The scores Q K^T are computed on the fp8 matrix cores from the codes

@@ -271,3 +271,24 @@ def test_transpose_rejects_malformed(fa):
         fa.transpose_block_lists(np.array([0, 1, 2], np.int32), np.array([0, 2], np.int32), 2)      # out of range
     empty = fa.transpose_block_lists(np.zeros(4, np.int32), np.zeros(0, np.int32), 3)
     assert np.array_equal(empty[0], np.zeros(4, np.int32)) and empty[1].size == 0
+
+
+def test_launch_work_item_limit(fa):
+    """Grids stay below 2^31 work-items: many tiny sequences, and a packed batch with one long
+    sequence among many, are rejected on the host although their row counts are allowed."""
+    no_dev = torch.cuda.device_count() == 0
+    accepted = 7 if no_dev else None     # past validation, then no device (FA_ERR_HIP)
+    # B*H = 2^30 sequences of one row: 2^30 rows (allowed) but 2^30 workgroups
+    assert call_fwd(fa, B=1 << 15, H=1 << 15, N=1) == 2
+    assert "work-items" in fa.lib.fa_last_error().decode()
+    # 1024 packed sequences, the longest 64K rows, 32 heads: 2.2M rows, 2^33 backward work-items
+    skew = dict(B=1024, H=32, H_kv=32, N=1 << 16, cu_seqlens=16, total=(1 << 16) + 1023)
+    assert call_attn_fwd(fa, make_desc(fa, **skew)) == 2
+    assert call_attn_bwd(fa, make_desc(fa, **skew)) == 2
+    assert "work-items" in fa.lib.fa_last_error().decode()
+    # exactly at the limit: 2^30 forward rows of 128K tokens (2^31 work-items) and 2^29
+    # backward rows (2^31); one more 256-row block of the forward is over
+    if no_dev:
+        assert call_fwd(fa, B=1, H=1 << 13, N=1 << 17) == accepted
+        assert call_attn_bwd(fa, make_desc(fa, B=1, H=1 << 12, H_kv=1 << 12, N=1 << 17), ws_bytes=1 << 32) == accepted
+    assert call_fwd(fa, B=1, H=(1 << 13) - 1, N=(1 << 17) + 256) == 2
