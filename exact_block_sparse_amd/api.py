@@ -43,6 +43,40 @@ def _check_inputs(*ts: torch.Tensor) -> None:
             raise ValueError(f"shape mismatch {tuple(t.shape)} vs {tuple(ts[0].shape)}")
 
 
+def _check_tensor_arg(name: str, t, shape, device, dtype=torch.bfloat16) -> None:
+    """A tensor the caller passes for the library to read or write (out, o, do): its dtype,
+    device and shape must be the ones the call implies, and its last dimension contiguous;
+    its other strides are passed to the library as they are. A wrong shape would otherwise
+    make the kernels read or write past the end of its storage."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dim() and t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name}: the head dimension must be contiguous (stride 1)")
+
+
+def _check_stats_arg(name: str, t, shape, device) -> None:
+    """Per-row statistics (lse): fp32, contiguous, of the given shape, on the device."""
+    _check_tensor_arg(name, t, shape, device, torch.float32)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(ws, need: int, device) -> tuple[torch.Tensor, int]:
+    """The backward workspace: a new one of `need` bytes, or the caller's (a contiguous tensor
+    on the device, its size counted in bytes)."""
+    if ws is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device), max(need, 1)
+    if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    return ws, ws.numel() * ws.element_size()
+
+
 def _empty_like_layout(t: torch.Tensor, dtype=None) -> torch.Tensor:
     """An uninitialised tensor with t's shape and, if t is a permuted dense tensor, its layout."""
     dtype = t.dtype if dtype is None else dtype
@@ -75,6 +109,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     B, H, N, d = q.shape
     o = _empty_like_layout(q) if out is None else out
     l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor_arg("out", o, q.shape, q.device)
+    _check_stats_arg("lse", l, (B, H, N), q.device)
     with torch.cuda.device(q.device):
         st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, N, d,
                         _strides(q), _strides(k), _strides(v), _strides(o), int(bool(causal)),
@@ -112,6 +148,8 @@ def sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_offsets, kv
     off, idx = _lists_to_device(kv_offsets, kv_indices, nb, causal, q.device)
     o = _empty_like_layout(q) if out is None else out
     l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor_arg("out", o, q.shape, q.device)
+    _check_stats_arg("lse", l, (B, H, N), q.device)
     with torch.cuda.device(q.device):
         st = lib.fa_sparse_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, N, d,
                                _strides(q), _strides(k), _strides(v), _strides(o), int(block_size),
@@ -128,17 +166,15 @@ def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
 def bwd(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None = None, workspace=None):
     """Backward through ``fa_bwd``; returns (dQ, dK, dV) bf16 in the layouts of q, k, v."""
     _check_inputs(q, k, v, o, do)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
     B, H, N, d = q.shape
+    _check_stats_arg("lse", lse, (B, H, N), q.device)
     dq, dk, dv = _empty_like_layout(q), _empty_like_layout(k), _empty_like_layout(v)
-    need = bwd_workspace_bytes(B, H, N, d)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    ws, ws_bytes = _workspace(workspace, bwd_workspace_bytes(B, H, N, d), q.device)
     with torch.cuda.device(q.device):
         st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                         B, H, N, d, _strides(q), _strides(k), _strides(v), _strides(o), _strides(do),
                         _strides(dq), _strides(dk), _strides(dv), int(bool(causal)), _scale(scale, d),
-                        _ptr(ws), ws.numel(), _stream(q.device))
+                        _ptr(ws), ws_bytes, _stream(q.device))
     check(st, "fa_bwd")
     return dq, dk, dv
 
@@ -304,6 +340,8 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool 
         o = out
     lshape = (H, total) if pk else (B, H, N)
     l = torch.empty(lshape, dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor_arg("out", o, q.shape, q.device)
+    _check_stats_arg("lse", l, lshape, q.device)
     S = _packed_strides if pk else _strides
     x = _desc(B, H, H_kv, N, d, causal, _scale(scale, d), cu, total, lists, fp8, (q_descale, k_descale, v_descale))
     with torch.cuda.device(q.device):
@@ -338,17 +376,19 @@ def attn_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None =
     if kv_offsets is not None:
         nb = (N + block_size - 1) // block_size
         lists = _device_lists(kv_offsets, kv_indices, q_offsets, q_indices, nb, causal, block_size, q.device, True)
+    _check_tensor_arg("o", o, q.shape, q.device)
+    _check_tensor_arg("do", do, q.shape, q.device)
+    _check_stats_arg("lse", lse, (H, total) if pk else (B, H, N), q.device)
     if pk:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv = _empty_like_layout(q), _empty_like_layout(k), _empty_like_layout(v)
     S = _packed_strides if pk else _strides
     x = _desc(B, H, H_kv, N, d, causal, _scale(scale, d), cu, total, lists)
-    need = int(lib.fa_attn_bwd_workspace_bytes(ctypes.byref(x)))
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    ws, ws_bytes = _workspace(workspace, int(lib.fa_attn_bwd_workspace_bytes(ctypes.byref(x))), q.device)
     with torch.cuda.device(q.device):
         st = lib.fa_attn_bwd(ctypes.byref(x), _ptr(q), S(q), _ptr(k), S(k), _ptr(v), S(v), _ptr(o), S(o), _ptr(do),
                              S(do), _ptr(lse), _ptr(dq), S(dq), _ptr(dk), S(dk), _ptr(dv), S(dv), _ptr(ws),
-                             ws.numel(), _stream(q.device))
+                             ws_bytes, _stream(q.device))
     check(st, "fa_attn_bwd")
     return dq, dk, dv

@@ -259,6 +259,51 @@ def test_sparse_backward_hand_lists_with_empty_block(fa):
     assert_close("dV", dv, dV, TOL_OUT)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_sparse_backward_lists_with_entries_above_the_diagonal(fa, d):
+    # Device lists in which query blocks also name key blocks above them: under causal
+    # masking those entries are skipped, so in the key-side lists a skipped query block comes
+    # before the diagonal one. The dK/dV pass must still take the diagonal steps with the
+    # causal element mask (key block 2 is listed by query blocks 0 (skipped), 2 and 4).
+    N = 128 * 5 - 30
+    w = W.small(1, 2, N, d, causal=True, seed=23, direction="bwd", sigma=0.5)
+    x = W.make_inputs(w)
+    g = dev(x)
+    lists = [[0, 2], [0, 1, 3], [1, 2], [0, 3, 4], [2, 4]]
+    off = np.cumsum([0] + [len(l) for l in lists]).astype(np.int32)
+    idx = np.array([k for l in lists for k in l], np.int32)
+    t_off, t_idx = fa.transpose_block_lists(off, idx, 5)
+    assert list(t_idx[t_off[2]:t_off[3]]) == [0, 2, 4]
+    to = lambda a: torch.from_numpy(a).to("cuda")
+    kw = dict(causal=True, scale=w.scale, kv_offsets=to(off), kv_indices=to(idx))
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], **kw)
+    dq, dk, dv = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], q_offsets=to(t_off), q_indices=to(t_idx), **kw)
+    torch.cuda.synchronize()
+    sp = dict(block=128, offsets=off, indices=idx)
+    dQ, dK, dV, O, L = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], causal=True, scale=w.scale,
+                                                 sparse=sp, return_forward=True)
+    assert_close("O", o, O, TOL_OUT)
+    assert_close("LSE", lse, L, TOL_LSE)
+    assert_close("dQ", dq, dQ, TOL_OUT)
+    assert_close("dK", dk, dK, TOL_OUT)
+    assert_close("dV", dv, dV, TOL_OUT)
+
+
+def test_wrappers_refuse_mis_shaped_outputs(fa):
+    w = W.small(1, 2, 200, 128, causal=True, seed=24, direction="bwd")
+    g = dev(W.make_inputs(w))
+    short = torch.empty(1, 2, 199, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        fa.fwd(g["q"], g["k"], g["v"], causal=True, out=short)
+    with pytest.raises(ValueError):
+        fa.attn_fwd(g["q"], g["k"], g["v"], causal=True, lse=torch.empty(1, 2, 100, device="cuda"))
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], causal=True)
+    with pytest.raises(ValueError):
+        fa.attn_bwd(g["q"], g["k"], g["v"], o[:, :, :100], lse, g["do"], causal=True)
+    with pytest.raises(TypeError):
+        fa.bwd(g["q"], g["k"], g["v"], o, lse.double(), g["do"], causal=True)
+
+
 def test_sparse_varlen_gqa_together(fa):
     lens = (300, 700, 129)
     w = W.small(H=4, d=128, causal=True, seed=21, H_kv=2, seqlens=lens, direction="bwd", sigma=0.5)
