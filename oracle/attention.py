@@ -38,8 +38,10 @@ taken here; H_kv = 1 is multi-query attention). In the backward a K/V head's gra
 the sum of the gradients its query heads send it, as the chain rule gives for a shared
 input.
 
-Variable-length batches (page 1, production notes on request batching and the FAQ on the
-varlen entry point: padding tokens are masked out of every softmax): sequences of
+Variable-length batches (page 1, section "The Production Pipeline: From Kernel to Service",
+on request batching: padding tokens are masked out of every tile's softmax; "How to Use
+Flash MSA Kernels for Long Context", FAQ on flash-batch inference, which points to a
+variable-length entry point): sequences of
 different lengths are packed one after another along the token axis, sequence b being
 rows cu_seqlens[b] .. cu_seqlens[b+1] - 1; each sequence attends only to itself, exactly
 as if it were run alone. ``attention_forward_varlen`` and ``attention_backward_varlen``

@@ -355,6 +355,30 @@ def _fwd_workload(fa, key, n_heads_checked=2, extra_rows=24):
     for (b, h) in heads:
         assert_close(f"O[{b},{h}]", o[b, h, rows], O_ref[b, h, rows], TOL_OUT)
         assert_close(f"LSE[{b},{h}]", lse[b, h, rows], L_ref[b, h, rows], TOL_LSE)
+    _fwd_every_head(x, o, lse, w, rng)
+
+
+def edge_rows(n: int, rng, extra: int = 1) -> list:
+    """First and last row of the first query block (the shortest causal rows) and of the
+    last one (the longest), the rows around the 256-row workgroup boundaries at the start
+    and the middle, and `extra` random rows."""
+    rows = {0, min(n - 1, 127), min(n - 1, 255), min(n - 1, 256), n // 2 - 1, n // 2, max(0, n - 128), n - 1}
+    rows.update(int(r) for r in rng.integers(0, n, size=extra))
+    return sorted(r for r in rows if 0 <= r < n)
+
+
+def _fwd_every_head(x, o, lse, w, rng):
+    """Every (sequence, head) pair of a full-size forward on a few rows each, so that a block
+    computed from another pair's rows, or left unwritten, fails in whichever pair it lands."""
+    Q, K, V = (f64(x[n]) for n in "qkv")     # fp64 once; the oracle then works on views
+    o_all, l_all = f64(o), f64(lse)
+    for b in range(w.B):
+        for h in range(w.H):
+            rows = edge_rows(w.N, rng)
+            O, L = oracle.attention_forward(Q[b:b + 1, h:h + 1], K[b:b + 1, h:h + 1], V[b:b + 1, h:h + 1],
+                                            causal=w.causal, scale=w.scale, sparse=w.sparse, rows=rows)
+            assert_close(f"O[{b},{h}] edge rows", o_all[b, h, rows], O[0, 0, rows], TOL_OUT)
+            assert_close(f"LSE[{b},{h}] edge rows", l_all[b, h, rows], L[0, 0, rows], TOL_LSE)
 
 
 def test_workload_dense_n512_d64_full(fa):
@@ -402,3 +426,18 @@ def test_workload_bwd_b2h32_n8k(fa):
     ref = oracle.backward_rows_dq(x["q"], x["k"], x["v"], x["do"], causal=True, scale=w.scale, b=0, h=3,
                                   rows=rows)
     assert_close("dQ rows", dq[0, 3, rows], np.stack([ref[int(r)] for r in rows]), TOL_OUT)
+    # every (sequence, head) pair: dQ on the edge rows, dK and dV on keys of the last two
+    # 64-key steps (few query rows see them, so the oracle stays fast)
+    rng = np.random.default_rng(55)
+    keys = [w.N - 1, w.N - 40, w.N - 64, w.N - 65]
+    Q, K, V, dO = (f64(x[n]) for n in ("q", "k", "v", "do"))
+    dq_all, dk_all, dv_all = f64(dq), f64(dk), f64(dv)
+    for b in range(w.B):
+        for h in range(w.H):
+            rows = edge_rows(w.N, rng)
+            ref = oracle.backward_rows_dq(Q, K, V, dO, causal=True, scale=w.scale, b=b, h=h, rows=rows)
+            assert_close(f"dQ[{b},{h}] edge rows", dq_all[b, h, rows], np.stack([ref[r] for r in rows]), TOL_OUT)
+            acc = oracle.backward_keys_dkdv(Q, K, V, dO, causal=True, scale=w.scale, b=b, h_kv=h, keys=keys,
+                                            rows=range(min(keys), w.N))
+            assert_close(f"dK[{b},{h}] keys", dk_all[b, h, keys], np.stack([acc[j][0] for j in keys]), TOL_OUT)
+            assert_close(f"dV[{b},{h}] keys", dv_all[b, h, keys], np.stack([acc[j][1] for j in keys]), TOL_OUT)

@@ -16,10 +16,10 @@ tensors of these shapes stand in for them.
 Five more cover the extensions: grouped K/V heads at the 32K shape and at the
 backward's shape (32 query heads over 8 K/V heads, the replication of the first page's
 GQA FAQ), a packed batch of variable-length sequences forward and backward (the first
-page's request batching; the pages give no length mix, so 16 lengths are drawn
+page's request batching in its production pipeline; the pages give no length mix, so 16 lengths are drawn
 uniformly from [256, 8192] with a seeded numpy generator), the backward of the
 128K block-sparse case (the third page's FAQ on training), and the 32K case with fp8
-(e4m3) inputs (the first page's FAQ on FP16 vs FP8): Q, K, V are drawn as for the bf16
+(e4m3) inputs (the second page's FAQ on FP16 vs FP8): Q, K, V are drawn as for the bf16
 case, then each tensor gets the usual per-tensor scaling, descale = amax / 448, and is
 stored as e4m3 codes of x / descale (torch's round-to-nearest-even conversion).
 
