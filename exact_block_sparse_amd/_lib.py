@@ -15,7 +15,7 @@ FA_STATUS = {
     5: "FA_ERR_LIST", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP", 8: "FA_ERR_ARG", 9: "FA_ERR_CAPACITY",
 }
 EXPORTS = ("fa_fwd", "fa_sparse_fwd", "fa_bwd_workspace_bytes", "fa_bwd", "fa_attn_fwd",
-           "fa_attn_bwd_workspace_bytes", "fa_attn_bwd", "fa_transpose_block_lists", "fa_make_block_lists",
+           "fa_attn_bwd_workspace_bytes", "fa_attn_bwd", "fa_attn_bwd_noalloc", "fa_transpose_block_lists", "fa_make_block_lists",
            "fa_check_block_lists", "fa_status_str", "fa_last_error")
 
 
@@ -66,6 +66,8 @@ def _load() -> ctypes.CDLL:
     lib.fa_attn_bwd_workspace_bytes.restype = sz
     lib.fa_attn_bwd.argtypes = [D, vp, S, vp, S, vp, S, vp, S, vp, S, vp, vp, S, vp, S, vp, S, vp, sz, vp]
     lib.fa_attn_bwd.restype = i32
+    lib.fa_attn_bwd_noalloc.argtypes = [D, vp, S, vp, S, vp, S, vp, S, vp, S, vp, vp, S, vp, S, vp, S, vp]
+    lib.fa_attn_bwd_noalloc.restype = i32
     lib.fa_transpose_block_lists.argtypes = [i64, pi32, pi32, i64, pi32, pi32]
     lib.fa_transpose_block_lists.restype = i32
     lib.fa_make_block_lists.argtypes = [i64, ctypes.c_int32, ctypes.c_int32, i32, i32, pi32, pi32, i64,

@@ -392,3 +392,43 @@ def attn_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None =
                              ws_bytes, _stream(q.device))
     check(st, "fa_attn_bwd")
     return dq, dk, dv
+
+
+NOALLOC_WORKSPACE_BYTES = 16 << 20   # FA_NOALLOC_WORKSPACE_BYTES of fa.h
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None = None, cu_seqlens=None,
+                     max_seqlen: int | None = None, kv_offsets=None, kv_indices=None, q_offsets=None,
+                     q_indices=None, block_size: int = BLOCK, dq=None, dk=None, dv=None):
+    """Backward through ``fa_attn_bwd_noalloc``: the function of ``attn_bwd`` with the workspace
+    the library owns (one per GPU), for callers that cannot allocate. Pass ``dq``, ``dk``, ``dv``
+    (shaped like q, k, v), device ``cu_seqlens`` and device block lists to make the call
+    allocate nothing on the Python side either; missing outputs are allocated here.
+    Calls that overlap on one GPU share the library's workspace and race.
+    """
+    packed = cu_seqlens is not None
+    _check_group(q, k, v, packed)
+    d = q.shape[-1]
+    H, H_kv = q.shape[1], k.shape[1]
+    pk, B, N, total, cu = _seq_args(q, cu_seqlens, max_seqlen)
+    lists = None
+    if kv_offsets is not None:
+        nb = (N + block_size - 1) // block_size
+        lists = _device_lists(kv_offsets, kv_indices, q_offsets, q_indices, nb, causal, block_size, q.device, True)
+    _check_tensor_arg("o", o, q.shape, q.device)
+    _check_tensor_arg("do", do, q.shape, q.device)
+    _check_stats_arg("lse", lse, (H, total) if pk else (B, H, N), q.device)
+    new = (lambda t: torch.empty_like(t)) if pk else _empty_like_layout
+    dq = new(q) if dq is None else dq
+    dk = new(k) if dk is None else dk
+    dv = new(v) if dv is None else dv
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_tensor_arg(name, t, like.shape, q.device)
+    S = _packed_strides if pk else _strides
+    x = _desc(B, H, H_kv, N, d, causal, _scale(scale, d), cu, total, lists)
+    with torch.cuda.device(q.device):
+        st = lib.fa_attn_bwd_noalloc(ctypes.byref(x), _ptr(q), S(q), _ptr(k), S(k), _ptr(v), S(v), _ptr(o), S(o),
+                                     _ptr(do), S(do), _ptr(lse), _ptr(dq), S(dq), _ptr(dk), S(dk), _ptr(dv), S(dv),
+                                     _stream(q.device))
+    check(st, "fa_attn_bwd_noalloc")
+    return dq, dk, dv

@@ -163,6 +163,20 @@ int check_lse(const float* lse) {
     return FA_OK;
 }
 
+// Tensors of a backward call.
+int check_bwd_tensors(const void* q, const fa_strides& sq, const void* k, const fa_strides& sk, const void* v,
+                      const fa_strides& sv, const void* o, const fa_strides& so, const void* dout,
+                      const fa_strides& sdo, const float* lse, const void* dq, const fa_strides& sdq, const void* dk,
+                      const fa_strides& sdk, const void* dv, const fa_strides& sdv) {
+    int st;
+    if ((st = check_tensor("q", q, sq)) || (st = check_tensor("k", k, sk)) || (st = check_tensor("v", v, sv)) ||
+        (st = check_tensor("o", o, so)) || (st = check_tensor("dout", dout, sdo)) ||
+        (st = check_tensor("dq", dq, sdq)) || (st = check_tensor("dk", dk, sdk)) ||
+        (st = check_tensor("dv", dv, sdv)) || (st = check_lse(lse)))
+        return st;
+    return FA_OK;
+}
+
 fa_attn_desc plain_desc(int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale) {
     fa_attn_desc x;
     std::memset(&x, 0, sizeof x);
@@ -223,11 +237,7 @@ int fa_attn_bwd(const fa_attn_desc* desc, const void* q, fa_strides sq, const vo
     if (st) return st;
     const fa_attn_desc& d = *desc;
     if (empty_problem(d)) return ok();
-    if ((st = check_tensor("q", q, sq)) || (st = check_tensor("k", k, sk)) || (st = check_tensor("v", v, sv)) ||
-        (st = check_tensor("o", o, so)) || (st = check_tensor("dout", dout, sdo)) ||
-        (st = check_tensor("dq", dq, sdq)) || (st = check_tensor("dk", dk, sdk)) ||
-        (st = check_tensor("dv", dv, sdv)) || (st = check_lse(lse)))
-        return st;
+    if ((st = check_bwd_tensors(q, sq, k, sk, v, sv, o, so, dout, sdo, lse, dq, sdq, dk, sdk, dv, sdv))) return st;
     const size_t need = fa_attn_bwd_workspace_bytes(desc);
     if (!workspace) return fail(FA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
     if (workspace_bytes < need)
@@ -255,6 +265,28 @@ int fa_attn_bwd(const fa_attn_desc* desc, const void* q, fa_strides sq, const vo
     a.q_indices = sparse ? or_other(d.q_indices, d.q_offsets) : nullptr;
     a.nnz = sparse ? d.nnz : 0;
     return launched(fa::launch_bwd(a, static_cast<hipStream_t>(stream)), "backward");
+}
+
+static_assert(FA_NOALLOC_WORKSPACE_BYTES == fa::kStaticWorkspaceBytes, "header and library disagree");
+
+int fa_attn_bwd_noalloc(const fa_attn_desc* desc, const void* q, fa_strides sq, const void* k, fa_strides sk,
+                        const void* v, fa_strides sv, const void* o, fa_strides so, const void* dout,
+                        fa_strides sdo, const float* lse, void* dq, fa_strides sdq, void* dk, fa_strides sdk,
+                        void* dv, fa_strides sdv, void* stream) {
+    int st = check_desc(desc, true);
+    if (st) return st;
+    if (empty_problem(*desc)) return ok();
+    if ((st = check_bwd_tensors(q, sq, k, sk, v, sv, o, so, dout, sdo, lse, dq, sdq, dk, sdk, dv, sdv))) return st;
+    const size_t need = fa_attn_bwd_workspace_bytes(desc);
+    if (need > fa::kStaticWorkspaceBytes)
+        return fail(FA_ERR_WORKSPACE, "the problem needs %zu bytes of workspace; the library-owned one holds %zu",
+                    need, fa::kStaticWorkspaceBytes);
+    if ((st = check_device())) return st;
+    void* ws = nullptr;
+    const hipError_t e = fa::static_workspace(&ws);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "library-owned workspace unavailable: %s", hipGetErrorString(e));
+    return fa_attn_bwd(desc, q, sq, k, sk, v, sv, o, so, dout, sdo, lse, dq, sdq, dk, sdk, dv, sdv, ws,
+                       fa::kStaticWorkspaceBytes, stream);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,

@@ -28,6 +28,8 @@
 // unpadded rows with XOR-swizzled 16-byte chunks (one K copy for both read patterns);
 // dq_kernel keeps a 272-byte row copy and a 320-byte transposed-read copy of K. Tiles are
 // fetched with raw buffer loads that zero-fill rows past N.
+#include <mutex>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -924,6 +926,37 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Library-owned backward workspace for callers that cannot allocate: one array per GPU,
+// held until the process ends. In host code `scratch` only names the array (it is not a
+// device address); its address on each device comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that address is ever handed to a kernel.
+// Every call on a GPU shares the array: calls that overlap on one GPU race on it.
+static __device__ __align__(256) unsigned char scratch[kStaticWorkspaceBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_workspace(void** ptr) {
+    *ptr = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     if (a.L.d == 64) return a.causal ? launch_all<64, true>(a, stream) : launch_all<64, false>(a, stream);

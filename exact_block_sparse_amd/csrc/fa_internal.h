@@ -70,4 +70,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // Launch the backward kernels on `stream`.
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
+// Size of the library-owned backward workspace (one per GPU).
+constexpr size_t kStaticWorkspaceBytes = (size_t)16 << 20;
+// Device address of the current device's library-owned workspace (set up on first use).
+hipError_t static_workspace(void** ptr);
+
 }  // namespace fa

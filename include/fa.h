@@ -265,6 +265,29 @@ FA_API int fa_attn_bwd(const fa_attn_desc* desc, const void* q, fa_strides sq, c
                        void* dv, fa_strides sdv, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_attn_bwd_noalloc - fa_attn_bwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation. Same
+ * arguments, function, kernels and results (bit for bit) as fa_attn_bwd, without the
+ * workspace: the per-row values D_i it needs live in a device array the library owns, one
+ * per GPU, of FA_NOALLOC_WORKSPACE_BYTES, held until the process ends. The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine). Its first call on a device
+ * looks up that device's array once (with the device current); later calls reuse it.
+ *
+ * Limit: problems whose workspace (fa_attn_bwd_workspace_bytes) exceeds
+ * FA_NOALLOC_WORKSPACE_BYTES, i.e. more than 4,194,304 (query head, row) pairs, return
+ * FA_ERR_WORKSPACE. The array is fully rewritten by every call before it is read, so no
+ * state carries over between calls, but every call on one GPU shares it: calls that
+ * overlap on one GPU (different streams, or threads without ordering) race and give wrong
+ * results; serialize them, e.g. on one stream.
+ * Errors as in fa_attn_bwd.
+ */
+#define FA_NOALLOC_WORKSPACE_BYTES ((size_t)16 << 20)
+FA_API int fa_attn_bwd_noalloc(const fa_attn_desc* desc, const void* q, fa_strides sq, const void* k, fa_strides sk,
+                               const void* v, fa_strides sv, const void* o, fa_strides so, const void* dout,
+                               fa_strides sdo, const float* lse, void* dq, fa_strides sdq, void* dk, fa_strides sdk,
+                               void* dv, fa_strides sdv, void* stream);
+
+/*
  * fa_transpose_block_lists - host: the key-side form of CSR block lists. For every key
  * block kb, t_indices[t_offsets[kb] .. t_offsets[kb+1]) lists in ascending order the query
  * blocks whose lists name kb (the walk the backward's dK/dV pass makes; "How Does
