@@ -27,28 +27,48 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2516.6     # 256 CUs x 4096 bf16 FLOP/clk x 2.4 GHz (AMD quotes 2.5 PFLOP/s dense)
+N_CU = 256
+BF16_FLOP_PER_CU_CLK = 4096
+SPEC_CLOCK_GHZ = 2.4
+PEAK_BF16_TFLOPS = N_CU * BF16_FLOP_PER_CU_CLK * SPEC_CLOCK_GHZ / 1e3   # 2516.6 (AMD quotes 2.5 PFLOP/s dense)
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS                                  # 5033.2 (AMD quotes 5.0 dense)
+# The fp8 forward runs Q.K^T (half the FLOPs) on the fp8 matrix cores and P.V in bf16: at
+# both peaks the time is F/2 / fp8 + F/2 / bf16, so its ceiling is the harmonic mean.
+PEAK_FP8_MIXED_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)   # 3355.5
 HBM_PEAK_GBS = 8000.0
+CPU_WORKERS_MAX = 16          # the host-core share of a one-GPU job
 HEADLINE = "causal_h32_n32k"
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_fwd_causal_h32_n32k.md")
+COUNTER_PROFILE = os.path.join(ROOT, "profiles", "mfma_lds_counters_fwd_causal_h32_n32k.md")
 FWD_SOURCE = os.path.join(ROOT, "exact_block_sparse_amd", "csrc", "fa_fwd.hip")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the headline kernel from the committed rocprofv3 summary
-    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the kernel source has changed
-    since the counters were taken."""
+def _profile_json(path):
+    """The JSON block of a committed rocprofv3 summary, or None when it is missing or the
+    headline kernel's source has changed since the counters were taken."""
     import hashlib
     try:
-        text = open(TRAFFIC_PROFILE).read()
-        blob = text.split("```json", 1)[1].split("```", 1)[0]
-        d = json.loads(blob)
+        text = open(path).read()
+        d = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
         cur = hashlib.sha256(open(FWD_SOURCE, "rb").read()).hexdigest()[:16]
     except (OSError, IndexError, ValueError):
         return None
-    return int(d["traffic_bytes"]) if d.get("source_sha256_16") == cur else None
+    return d if d.get("source_sha256_16") == cur else None
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline kernel (FETCH_SIZE + WRITE_SIZE, copy-calibrated)."""
+    d = _profile_json(TRAFFIC_PROFILE)
+    return int(d["traffic_bytes"]) if d else None
+
+
+def measured_clock_ghz():
+    """Shader clock of the headline kernel under load: GRBM_GUI_ACTIVE cycles (summed over
+    the 8 XCDs, so divided by 8) per second of dispatch, from the committed counter run."""
+    d = _profile_json(COUNTER_PROFILE)
+    return float(d["clock_ghz"]) if d and d.get("clock_ghz") else None
 
 
 def log(msg: str) -> None:
@@ -187,6 +207,9 @@ def summarize(info, t):
                ms_min=round(t["min_ms"], 4), reps=t["reps"], tflops=round(tflops, 2),
                pct_peak=round(100 * tflops / PEAK_BF16_TFLOPS, 2), flops=info["flops"],
                algorithmic_bytes=info["bytes"])
+    if info["workload"].dtype == "fp8_e4m3":
+        out["pct_of_mixed_fp8_bf16_peak"] = round(100 * tflops / PEAK_FP8_MIXED_TFLOPS, 2)
+        out["mixed_fp8_bf16_peak"] = round(PEAK_FP8_MIXED_TFLOPS, 1)
     if "flops_exact" in info:
         out["flops_element_exact"] = info["flops_exact"]
         out["tflops_element_exact"] = round(info["flops_exact"] / (ms * 1e-3) / 1e12, 2)
@@ -194,39 +217,88 @@ def summarize(info, t):
     return out
 
 
-def cpu_baseline(W, x_cpu, seconds_target: float = 15.0):
-    """The oracle as it stands, on the host cores, over a bounded sample of the headline
-    workload: whole query rows of head (0, 0), spread across the sequence, one process per
-    core. Reported as TFLOP/s over the sampled rows' algorithmic FLOPs (4 * keys * d each)."""
-    import multiprocessing as mp
-    import numpy as np
-    import torch
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    w = W.WORKLOADS[HEADLINE]
-    cores = min(os.cpu_count() or 1, 16)
-    rng = np.random.default_rng(0)
-    # Row i of a causal head costs 4*(i+1)*d FLOP. Pick rows for ~seconds_target of work at
-    # ~1 GFLOP/s per core (the row-at-a-time fp64 oracle's rough rate), then time them.
-    budget = seconds_target * 1.0e9 * cores
+
+def cpu_head(w, x):
+    """Head (0, 0) of a workload's CPU inputs as fp64 numpy [1, 1, n, d] arrays (the first
+    sequence when packed): the sample the CPU baseline times."""
+    import torch
+    out = {}
+    for n in ("q", "k", "v", "do"):
+        if n not in x:
+            continue
+        t = x[n]
+        if w.packed:
+            t = t[: int(w.seqlens[0]), 0:1].transpose(0, 1)[None]
+        else:
+            t = t[0:1, 0:1]
+        t = t.to(torch.float64)
+        if w.dtype == "fp8_e4m3":
+            t = t * x[n + "_descale"]
+        out[n] = t.contiguous().numpy()
+    return out
+
+
+def _sample_rows(w, n, kind, budget_flop, rng):
+    """Random query rows of head (0, 0) until the oracle FLOP of the sample reach the budget;
+    a row with J allowed keys costs 4*J*d FLOP forward and 6*J*d for a dQ row (scores, dP,
+    dQ)."""
+    import oracle
+    ks = oracle.KeySets(n, w.causal, w.sparse)
+    per = 6 if kind == "dq" else 4
     rows, flop = [], 0.0
-    for r in rng.permutation(w.N):
-        f = 4.0 * (int(r) + 1) * w.d
-        if flop + f > budget:
+    for r in rng.permutation(n):
+        f = per * len(ks.keys(int(r))) * w.d
+        if rows and flop + f > budget_flop:
             break
         rows.append(int(r))
         flop += f
-    rows = sorted(rows)
-    _CPU_STATE["w"] = w
-    _CPU_STATE["x"] = {n: x_cpu[n][0:1, 0:1].to(torch.float64).numpy() for n in "qkv"}
-    chunks = [rows[i::cores] for i in range(cores)]
+    return sorted(rows), flop
+
+
+def cpu_baseline(samples, seconds_target: float = 15.0, per_workload_seconds: float = 2.5):
+    """The oracle as it stands, timed on the host cores over bounded samples of the workloads:
+    whole query rows of head (0, 0) (forward rows; for a backward workload, the oracle's
+    per-row dQ), spread over the sequence, one process per core (at most the 16-core share
+    of a one-GPU job). The headline's sample is about `seconds_target` seconds of CPU work;
+    the others about `per_workload_seconds` each. Reported as TFLOP/s over the FLOP the
+    oracle performs for the sampled rows, and as rows/s."""
+    import multiprocessing as mp
+    import numpy as np
+
+    cores = max(1, min(os.cpu_count() or 1, CPU_WORKERS_MAX))
+    rate = 0.5e9   # rough per-core fp64 rate of the row-at-a-time oracle, to size the samples
     ctx = mp.get_context("fork")
-    with ctx.Pool(cores) as pool:
-        t0 = time.perf_counter()
-        pool.map(_cpu_rows, chunks)
-        dt = time.perf_counter() - t0
-    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(rows)} random query rows of head (0,0) of {w.describe()}; "
-                      f"{flop:.3e} FLOP in {dt:.1f} s (fp64 numpy, row at a time, one process per core)"}
+    results = {}
+    for key, (w, head) in samples.items():
+        kind = "dq" if w.direction in ("bwd", "sparse_bwd") else "fwd"
+        n = head["q"].shape[2]
+        secs = seconds_target if key == HEADLINE else per_workload_seconds
+        rows, flop = _sample_rows(w, n, kind, secs * rate * cores, np.random.default_rng(0))
+        _CPU_STATE.clear()
+        _CPU_STATE.update(w=w, x=head, kind=kind)
+        with ctx.Pool(cores) as pool:
+            t0 = time.perf_counter()
+            pool.map(_cpu_rows, [rows[i::cores] for i in range(cores)])
+            dt = time.perf_counter() - t0
+        what = "per-row dQ of the backward" if kind == "dq" else "forward rows"
+        results[key] = {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "rows": len(rows),
+                        "rows_per_s": round(len(rows) / dt, 1), "seconds": round(dt, 2),
+                        "sample": f"{len(rows)} random {what} of head (0,0) of {w.describe()}; "
+                                  f"{flop:.3e} FLOP"}
+    head = results[HEADLINE]
+    return {"value": head["value"], "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": head["sample"] + f" in {head['seconds']} s (fp64 numpy, row at a time, one process "
+                                       f"per core)",
+            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(), "per_workload": results}
 
 
 _CPU_STATE = {}
@@ -236,8 +308,12 @@ def _cpu_rows(rows):
     from threadpoolctl import threadpool_limits
     threadpool_limits(1)
     import oracle
-    w, x = _CPU_STATE["w"], _CPU_STATE["x"]
-    oracle.attention_forward(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale, rows=rows)
+    w, x, kind = _CPU_STATE["w"], _CPU_STATE["x"], _CPU_STATE["kind"]
+    if kind == "dq":
+        oracle.backward_rows_dq(x["q"], x["k"], x["v"], x["do"], causal=w.causal, scale=w.scale, sparse=w.sparse,
+                                rows=rows)
+    else:
+        oracle.attention_forward(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale, sparse=w.sparse, rows=rows)
     return len(rows)
 
 
@@ -283,6 +359,11 @@ def main():
     log(f"[bench] {HEADLINE}: {hs['ms_mean']} ms, {hs['tflops']} TFLOP/s ({hs['pct_peak']}% of peak)")
     w = head["workload"]
     achieved = head["flops"] / (t["mean_ms"] * 1e-3) / 1e12
+    # the CPU baseline times the oracle on head (0, 0) of the five benchmark configurations
+    cpu_samples = {}
+    want_cpu = not args.no_cpu_baseline
+    if want_cpu:
+        cpu_samples[HEADLINE] = (w, cpu_head(w, head["x"]))
 
     others = {}
     if args.workloads != "headline":
@@ -297,7 +378,9 @@ def main():
                 others[key] = hs
                 continue
             info = prepare(fa, W, torch, key)
-            reps = 50 if key == "dense_n512_d64" else 10
+            if want_cpu and key in W.BENCHMARK_CONFIGS:
+                cpu_samples[key] = (info["workload"], cpu_head(info["workload"], info["x"]))
+            reps = 50 if key == "dense_n512_d64" else max(20, args.steps)
             tt = timer.run(info["fn"], reps, 3)
             others[key] = summarize(info, tt)
             log(f"[bench] {key}: {others[key]['ms_mean']} ms, {others[key]['tflops']} TFLOP/s")
@@ -307,8 +390,11 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu_baseline: timing the oracle on host cores")
-        cpu = cpu_baseline(W, head["x"])
-        log(f"[bench] cpu_baseline: {cpu['value']} TFLOP/s on {cpu['cores']} cores")
+        del head["x"]
+        cpu = cpu_baseline(cpu_samples)
+        log(f"[bench] cpu_baseline: {cpu['value']} TFLOP/s on {cpu['cores']} cores ({cpu['cpu_model']}); "
+            + ", ".join(f"{k} {v['rows_per_s']} rows/s" for k, v in cpu["per_workload"].items()))
+    clock = measured_clock_ghz()
 
     line = {
         "metric": "attention TFLOP/s (bf16 fwd/bwd, causal & block-sparse) and % of MFMA peak on 1 GPU",
@@ -330,7 +416,12 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(), "algorithmic_bytes": head["bytes"],
                      "kernel": "fwd_pingpong_dma_kernel<causal>", "per_launch_flop": head["flops"],
-                     "avg_launch_ms": round(t["mean_ms"], 4)},
+                     "avg_launch_ms": round(t["mean_ms"], 4),
+                     # the same achieved rate against the peak at the shader clock measured under
+                     # this kernel's load (GRBM_GUI_ACTIVE, committed counter run), not 2.4 GHz
+                     "clock_ghz_measured": clock,
+                     "pct_of_measured_clock_peak": (round(100 * achieved / (N_CU * BF16_FLOP_PER_CU_CLK * clock / 1e3),
+                                                          2) if clock else None)},
         "cpu_baseline": cpu,
         "workloads": others,
         "context": "pages' claim: FlashAttention-2 2-4x faster than cuDNN attention on one A100 beyond 8K "

@@ -132,6 +132,8 @@ def to_fp8(x: torch.Tensor):
     descale = float(torch.tensor(amax / FP8_MAX if amax > 0 else 1.0, dtype=torch.float32))
     return (x / descale).to(torch.float8_e4m3fn), descale
 ORDER = list(WORKLOADS)
+# the five benchmark configurations (the rest are the extensions)
+BENCHMARK_CONFIGS = ("dense_n512_d64", "causal_b4h32_n4k_bnhd", "causal_h32_n32k", "sparse_h16_n128k", "bwd_b2h32_n8k")
 
 
 def physical_shape(w: Workload) -> tuple:
