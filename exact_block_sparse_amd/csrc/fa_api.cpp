@@ -225,7 +225,7 @@ size_t fa_attn_bwd_workspace_bytes(const fa_attn_desc* desc) {
     if (!desc || desc->B <= 0 || desc->H <= 0 || desc->N <= 0) return 0;
     const int64_t rows = packed(*desc) ? desc->total : desc->B * desc->N;
     if (rows <= 0) return 0;
-    const size_t bytes = (size_t)desc->H * (size_t)rows * sizeof(float);
+    const size_t bytes = 2 * (size_t)desc->H * (size_t)rows * sizeof(float);   // D and the exp2-domain LSE
     return (bytes + 255) & ~(size_t)255;
 }
 

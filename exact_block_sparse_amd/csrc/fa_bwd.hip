@@ -88,11 +88,15 @@ struct Tile {
     }
 };
 
-// ----------------------------------------------------------------------------- D = rowsum(dO * O)
+// ----------------------------------------------------------------------------- -D = -rowsum(dO * O)
+// Writes -D (negated: it then starts the dP accumulators of the dK/dV pass, which yields dP - D
+// with no subtraction) and each row's LSE in the exp2 domain, lse2 = LSE log2(e), with -inf (a
+// row with no allowed key) as +inf so that its probabilities exp2(s - lse2) are exactly 0.
 template <int D>
 __global__ __launch_bounds__(kThreads) void pre_kernel(const uint16_t* o, int64_t osb, int64_t osh, int64_t osn,
                                                        const uint16_t* dout, int64_t dsb, int64_t dsh, int64_t dsn,
-                                                       float* delta, int H, int N, int64_t rows) {
+                                                       const float* lse, float* delta, float* lse2, int H, int N,
+                                                       int64_t rows) {
     constexpr int LPR = D / 8;                       // lanes per row, 8 elements each
     constexpr int RPB = kThreads / LPR;              // rows per block
     const int tid = threadIdx.x;
@@ -116,7 +120,11 @@ __global__ __launch_bounds__(kThreads) void pre_kernel(const uint16_t* o, int64_
         }
 #pragma unroll
         for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-        if (row < rows && part == 0) delta[row] = acc;
+        if (row < rows && part == 0) {
+            delta[row] = -acc;   // stored negated: -D starts the dP accumulators of the dK/dV pass
+            const float l = lse[row];
+            lse2[row] = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e;
+        }
     }
 }
 
@@ -127,6 +135,7 @@ struct KVParams {
     const uint16_t *q, *k, *v, *dout;
     const float* lse;
     const float* delta;
+    const float* lse2;     // LSE * log2(e), -inf as +inf (written by pre_kernel), laid out like delta
     uint16_t *dk, *dv;
     int64_t qsb, qsh, qsn, ksb, ksh, ksn, vsb, vsh, vsn, dsb, dsh, dsn;
     int64_t dksb, dksh, dksn, dvsb, dvsh, dvsn;
@@ -172,6 +181,95 @@ __device__ __forceinline__ f32x4v mfma16(bf16x8 a, bf16x8 b, f32x4v c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// The query steps a key block's dK/dV pass walks: 64-row query tiles, for each of the G
+// query heads that read the block's K/V head in turn. Dense: the tiles from the first one
+// that can see these keys (causal) or from 0 to the end. Block-sparse: both halves of every
+// query block the key-side list names for this key block. Under causal masking only the
+// steps of the diagonal block hold keys after queries: the first two of each query head
+// (dense), or the two halves of the list's diagonal entry (block-sparse: the first entry not
+// below the key block, the lists being ascending; entries before it are above-diagonal
+// entries of the query-side lists, which are skipped). Those steps are numbered first, so
+// the others need no element test. Out-of-range list entries (or, causal, entries above the
+// diagonal) become an empty tile at row N, whose loads are zero-filled.
+template <bool CAUSAL>
+struct KvSteps {
+    int n_all;     // steps of all query heads
+    int n_mask;    // the first n_mask steps need the causal element mask
+    int m_per, u_per, diag, t0, nqb, kblk, hk, G, N;
+    int64_t lo;
+    bool sparse;
+    const int32_t* qi;
+
+    __device__ void init(const KVParams& p, int kblk_, int hk_, int N_, int k0) {
+        kblk = kblk_;
+        hk = hk_;
+        G = p.G;
+        N = N_;
+        qi = p.q_indices;
+        const int nsteps = (N + kStep - 1) / kStep;
+        t0 = CAUSAL ? k0 / kStep : 0;
+        lo = 0;
+        int64_t hi = 0;
+        sparse = p.q_offsets != nullptr;
+        if (sparse) {
+            lo = load_uniform(p.q_offsets, kblk);
+            hi = load_uniform(p.q_offsets, kblk + 1);
+            lo = lo < 0 ? 0 : (lo > p.nnz ? p.nnz : lo);
+            hi = hi < lo ? lo : (hi > p.nnz ? p.nnz : hi);
+        }
+        const int per = sparse ? (int)(2 * (hi - lo)) : nsteps - t0;
+        n_all = per * G;
+        nqb = (N + kKV_BK - 1) / kKV_BK;
+        m_per = 0;   // masked steps per query head: 0, 2, or 1 when a head has a single step
+        diag = 0;    // block-sparse: list position (from lo) of the diagonal entry
+        if constexpr (CAUSAL) {
+            if (sparse) {
+                int64_t e = lo;
+                while (e < hi && load_uniform(qi, e) < kblk) ++e;
+                if (e < hi && load_uniform(qi, e) == kblk) {
+                    m_per = 2;
+                    diag = (int)(e - lo);
+                }
+            } else {
+                m_per = min(2, per);
+            }
+        }
+        n_mask = m_per * G;
+        u_per = per - m_per;
+    }
+
+    // First row of step s (N past the last step or for a skipped entry); hq: its query head.
+    __device__ int row(int s, int& hq) const {
+        if (s >= n_all) {
+            hq = hk * G;
+            return N;
+        }
+        int gq = 0, j = 0;   // query head in the group; step within that head's sequence
+        bool masked_step = false;
+        if constexpr (CAUSAL) {
+            if (s < n_mask) {
+                gq = s / m_per;
+                j = s - gq * m_per;
+                masked_step = true;
+            }
+        }
+        if (!masked_step) {
+            const int u = s - n_mask;
+            gq = u / u_per;
+            j = u - gq * u_per;   // among the unmasked steps
+        }
+        hq = hk * G + gq;
+        if (!sparse) return (t0 + (masked_step ? j : m_per + j)) * kStep;
+        int e = j >> 1;   // list entry (from lo): the diagonal one, or the others in order
+        if (masked_step) e = diag;
+        else if (m_per && e >= diag) ++e;
+        const int qb = load_uniform(qi, lo + e);
+        if (qb < 0 || qb >= nqb || (CAUSAL && qb < kblk)) return N;
+        const int r0 = qb * kKV_BK + (j & 1) * kStep;
+        return r0 < N ? r0 : N;
+    }
+};
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
     using L = KVCfg<D>;
@@ -214,74 +312,10 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
         dv[cb] = f32x4v{};
     }
 
-    // Steps: 64-row query tiles, for each of the G query heads that read this K/V head in
-    // turn. Dense: the tiles from the first one that can see these keys (causal) or from 0 to
-    // the end. Block-sparse: both halves of every query block the key-side list names for
-    // this key block. Under causal masking only the steps of the diagonal block hold keys
-    // after queries: the first two of each query head (dense), or the two halves of the
-    // list's diagonal entry (block-sparse: the first entry not below the key block, the lists
-    // being ascending; entries before it are above-diagonal entries of the query-side lists,
-    // which are skipped). Those steps are taken first, so the others run without the element
-    // test. Out-of-range list entries (or, causal, entries above the diagonal) become an empty
-    // tile at row N: zero-filled loads, LSE = +inf, so their probabilities are exactly 0.
-    const int nsteps = (N + kStep - 1) / kStep;
-    const int t0 = CAUSAL ? k0 / kStep : 0;
-    int64_t lo = 0, hi = 0;
-    const bool sparse = p.q_offsets != nullptr;
-    if (sparse) {
-        lo = load_uniform(p.q_offsets, kblk);
-        hi = load_uniform(p.q_offsets, kblk + 1);
-        lo = lo < 0 ? 0 : (lo > p.nnz ? p.nnz : lo);
-        hi = hi < lo ? lo : (hi > p.nnz ? p.nnz : hi);
-    }
-    const int per = sparse ? (int)(2 * (hi - lo)) : nsteps - t0;
-    const int n_all = per * p.G;
-    const int nqb = (N + kKV_BK - 1) / kKV_BK;
-    int m_per = 0;      // masked steps per query head: 0, 2, or 1 when a head has a single step
-    int diag = 0;       // block-sparse: list position (from lo) of the diagonal entry
-    if constexpr (CAUSAL) {
-        if (sparse) {
-            int64_t e = lo;
-            while (e < hi && load_uniform(p.q_indices, e) < kblk) ++e;
-            if (e < hi && load_uniform(p.q_indices, e) == kblk) {
-                m_per = 2;
-                diag = (int)(e - lo);
-            }
-        } else {
-            m_per = min(2, per);
-        }
-    }
-    const int n_mask = m_per * p.G;
-    const int u_per = per - m_per;
-    auto step_row = [&](int s, int& hq) -> int {   // first row of step s; N past the last step
-        if (s >= n_all) {
-            hq = hk * p.G;
-            return N;
-        }
-        int gq = 0, j = 0;   // query head in the group; step within that head's sequence
-        bool masked_step = false;
-        if constexpr (CAUSAL) {
-            if (s < n_mask) {
-                gq = s / m_per;
-                j = s - gq * m_per;
-                masked_step = true;
-            }
-        }
-        if (!masked_step) {
-            const int u = s - n_mask;
-            gq = u / u_per;
-            j = u - gq * u_per;   // among the unmasked steps
-        }
-        hq = hk * p.G + gq;
-        if (!sparse) return (t0 + (masked_step ? j : m_per + j)) * kStep;
-        int e = j >> 1;   // list entry (from lo): the diagonal one, or the others in order
-        if (masked_step) e = diag;
-        else if (m_per && e >= diag) ++e;
-        const int qb = load_uniform(p.q_indices, lo + e);
-        if (qb < 0 || qb >= nqb || (CAUSAL && qb < kblk)) return N;
-        const int r0 = qb * kKV_BK + (j & 1) * kStep;
-        return r0 < N ? r0 : N;
-    };
+    KvSteps<CAUSAL> steps;
+    steps.init(p, kblk, hk, N, k0);
+    const int n_all = steps.n_all, n_mask = steps.n_mask;
+    auto step_row = [&](int s, int& hq) -> int { return steps.row(s, hq); };
     const float c = p.c;
 
     // Staging in two register sets: the loads of step t + 2 are issued at the start of step t
@@ -356,7 +390,7 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
                 float pe = fast_exp2(fmaf(a.s[tt][r], c, -l4[r]));
                 if (mask && key > qt0 + q0 + 4 * g + r) pe = 0.0f;
                 pv[4 * tt + r] = pe;
-                dsv[4 * tt + r] = pe * (a.p[tt][r] - d4[r]);
+                dsv[4 * tt + r] = pe * (a.p[tt][r] + d4[r]);   // d4 = -D
             }
         }
         pb = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
@@ -461,6 +495,400 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
     }
 }
 
+// ----------------------------------------------------------------------------- dK, dV, head dimension 128
+// A workgroup owns 128 keys in four groups of 32. Each group is served by a pair of waves
+// that share the staged Q and dO tiles and split the group's four products:
+// * the P wave (waves 0-3) computes S = Q K^T, P = exp2(S scale log2(e) - LSE log2(e)) and
+//   dV^T += dO^T P, and hands P to its partner through LDS as fp16 (P <= 1; rounding to
+//   nearest loses at most 2^-11 of it, a quarter of what bf16 would, so dS = P (dP - D)
+//   keeps nearly the accuracy of an fp32 P, which would not fit the LDS budget);
+// * the dS wave (waves 4-7), one step behind, computes dS = P o (dP - D) and dK^T += Q^T dS,
+//   and then dP - D of the step the P wave is on (its accumulators start at -D), kept in
+//   registers for the next iteration.
+// Every product is a 32x32x16 one with the lane's key as its column: K (P wave) or V (dS
+// wave) rows of the key are register B operands of S and dP, whose accumulators (rows =
+// queries) turn into the B operands of the gradient products without any exchange between
+// lanes; Q and dO rows (S, dP) and their transposes (dV, dK, via ds_read_b64_tr_b16) come
+// from one unpadded copy of each tile whose 16-byte chunks are XOR-swizzled so that both
+// read patterns are free of bank conflicts. Against 16 keys per wave on 16x16x32 products,
+// this reads a quarter of the LDS bytes per product.
+//
+// An iteration t has two barriers. Before the first, the P waves run S(t) on the matrix
+// cores while the dS waves read P(t - 1) and form dS; after it, the P waves form P(t) (and
+// overwrite the single exchange buffer) and issue the loads of step t + 2 while the dS waves
+// run dK(t - 1) and dP(t); then the P waves run dV(t). So the vector work of each kind of
+// wave sits beside the other's matrix products. Tiles travel from memory straight into LDS
+// (four stages: the P waves read step t, the dS waves step t - 1, steps t + 1 and t + 2 are
+// loading), with the step's LSE (pre-converted to the exp2 domain by pre_kernel) and -D rows.
+// Only the dS waves load, right before the first barrier, where they would otherwise wait
+// for the P waves' S products: issuing the loads of a step stalls a wave for hundreds of
+// cycles while the address path works through them, and there it costs nothing. Product
+// phases run at raised wave priority, so that they issue ahead of the neighbour's vector
+// work. Rows past the sequence end read as zeros, which makes their contributions exactly 0
+// (zero dO rows for dV; dP = 0 and D = 0 for dK).
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+constexpr int kPairStages = 4;
+constexpr int kPairStatB = 2 * kStep * 4;                      // lse2[64], -D[64]
+constexpr int kPairStageB = 2 * kLdsTileB + kPairStatB;       // Q | dO | lse2 | -D
+constexpr int kPairXB = 4 * kStep * 32 * 2;                   // P of one step for four key groups, fp16
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(KVParams p) {
+    constexpr int D = 128;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kPairStages * kPairStageB + kPairXB];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, i = lane & 31;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const bool pwave = wave_u < 4;   // uniform per wave
+    const int grp = wave_u & 3;
+    // Block-sparse: plain order, so that all XCDs work on the same head at once and its
+    // Q/dO stay in the cache they share (key-side lists reach across the whole head).
+    const int logical = p.q_offsets ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
+    const int bhk = logical / p.nkb, kblk = logical % p.nkb;   // ascending: longest first under causal
+    const int hk = bhk / p.B, b = bhk % p.B;   // head-major: an XCD's share spans every sequence
+    const SeqSpan sp = seq_span(p.cu, p.total, b, p.N);
+    const int N = sp.len;
+    const int k0 = kblk * kKV_BK;
+    if (k0 >= N) return;   // past the end of a shorter packed sequence (uniform per workgroup)
+    const int key = k0 + 32 * grp + i;
+
+    // K (P waves) or V (dS waves) of the lane's key: k-step ks holds d = 16 ks + 8 hf .. + 7.
+    bf16x8 kv[D / 16];
+    {
+        const uint16_t* base = pwave ? p.k + seq_off(sp, b, hk, p.ksb, p.ksh, p.ksn) + (int64_t)key * p.ksn
+                                     : p.v + seq_off(sp, b, hk, p.vsb, p.vsh, p.vsn) + (int64_t)key * p.vsn;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) kv[ks] = as_bf16x8(load16(base + 16 * ks + 8 * hf, key < N));
+    }
+    f32x16 acc[D / 32];   // dV^T (P waves) or dK^T (dS waves): row = head-dimension column, column = key
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
+
+    KvSteps<CAUSAL> steps;
+    steps.init(p, kblk, hk, N, k0);
+    const int n_all = steps.n_all, n_mask = steps.n_mask, m_per = steps.m_per, u_per = steps.u_per;
+    const float c = p.c;
+
+    // Per-lane LDS byte offsets within a tile: row reads (row i, chunk 2 ks + hf) and
+    // transposing reads (per 32-column block cb, for the lane's row and the row 8 below it),
+    // both in the kSwzBoth layout.
+    uint32_t ar[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) ar[ks] = (uint32_t)(i * kLdsRowB + 16 * ((2 * ks + hf) ^ swz<kSwzBoth>(i)));
+    uint32_t at[D / 32][2];
+    {
+        const int g16 = (lane >> 4) & 1, j16 = lane & 15;
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+            const int row = 4 * hf + (j16 >> 2) + 8 * h8;
+#pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb) {
+                const int chunk = 4 * cb + 2 * g16 + ((j16 & 3) >> 1);
+                at[cb][h8] = (uint32_t)(row * kLdsRowB + 16 * (chunk ^ swz<kSwzBoth>(row)) + 8 * (j16 & 1));
+            }
+        }
+    }
+    const uint32_t lds0 = lds_address(smem);
+    const uint32_t xbuf = lds0 + kPairStages * kPairStageB;
+    // The P wave reads Q rows and dO transposes, the dS wave dO rows and Q transposes; the P
+    // wave reads the lse2 row of a stage, the dS wave the -D row (16 bytes per lane group of four
+    // queries: 4 hf + 32 m + 8 j).
+    const uint32_t row_tile = pwave ? 0u : (uint32_t)kLdsTileB;
+    const uint32_t tr_tile = pwave ? (uint32_t)kLdsTileB : 0u;
+    const uint32_t stat_lane = 2 * kLdsTileB + (pwave ? 0u : (uint32_t)(kStep * 4)) + 16 * hf;
+    // the lane's 16-byte slot of the exchange buffer for (group, half m, k-step st)
+    const uint32_t xlane = (uint32_t)(grp * 4 * 1024 + 16 * lane);
+
+    // Loads (dS waves only): each dS wave fetches four of the sixteen 1-KB pieces (four rows
+    // each) of both the Q and the dO tile; wave 4 also the lse2 row, wave 5 the -D row. The
+    // steps are walked in order with an iterator: the query head changes only at the end of a
+    // run (a head's masked steps, then its unmasked ones), so the per-head bases move by one
+    // add then.
+    const int G = p.G;
+    const int h0 = hk * G;
+    const uint32_t qsn2 = (uint32_t)(2 * p.qsn), dsn2 = (uint32_t)(2 * p.dsn);   // row strides in bytes
+    const unsigned char* const q_head0 = reinterpret_cast<const unsigned char*>(p.q + seq_off(sp, b, h0, p.qsb, p.qsh, p.qsn));
+    const unsigned char* const d_head0 =
+        reinterpret_cast<const unsigned char*>(p.dout + seq_off(sp, b, h0, p.dsb, p.dsh, p.dsn));
+    const float* const st_head0 = (wave_u == 4 ? p.lse2 : p.delta) + seq_stat_off(sp, b, h0, p.H, p.N, p.total);
+    const int64_t st_dh = sp.packed ? p.total : (int64_t)p.N;   // statistics stride between heads
+    const unsigned char* ld_q = q_head0;
+    const unsigned char* ld_d = d_head0;
+    const float* ld_st = st_head0;
+    uint32_t qoff[4], doff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = 4 * (4 * grp + j) + (lane >> 4), slot = lane & 15;
+        const uint32_t sw = 16 * (slot ^ swz<kSwzBoth>(row));
+        qoff[j] = (uint32_t)row * qsn2 + sw;
+        doff[j] = (uint32_t)row * dsn2 + sw;
+    }
+    const uint32_t lds_piece = 4096u * (uint32_t)grp;
+    const bool stat_wave = wave_u == 4 || wave_u == 5;
+    const uint32_t lds_stat = 2 * kLdsTileB + (uint32_t)((wave_u - 4) * kStep * 4);
+    int ld_gq = 0, ld_j = 0;
+    bool ld_masked = m_per > 0;
+    auto issue_next = [&](uint32_t stage) {
+        // first row of the step at (ld_masked, ld_gq, ld_j); N for a skipped list entry
+        int r0;
+        if (!steps.sparse) {
+            r0 = (steps.t0 + (ld_masked ? ld_j : m_per + ld_j)) * kStep;
+        } else {
+            int e = ld_j >> 1;
+            if (ld_masked) e = steps.diag;
+            else if (m_per && e >= steps.diag) ++e;
+            const int qb = load_uniform(steps.qi, steps.lo + e);
+            r0 = (qb < 0 || qb >= steps.nqb || (CAUSAL && qb < kblk)) ? N : qb * kKV_BK + (ld_j & 1) * kStep;
+            r0 = r0 < N ? r0 : N;
+        }
+        const int rows = min(N - r0, kStep);   // rows of the tile inside the sequence (<= 0: none)
+        const uint64_t qb64 = reinterpret_cast<uint64_t>(ld_q) + (uint64_t)(uint32_t)r0 * qsn2;
+        const uint64_t db64 = reinterpret_cast<uint64_t>(ld_d) + (uint64_t)(uint32_t)r0 * dsn2;
+        i32x4 rq, rd;
+        rq[0] = (int)(uint32_t)qb64;
+        rq[1] = (int)((uint32_t)(qb64 >> 32) & 0xffffu);
+        rq[2] = rows > 0 ? (int)((uint32_t)(rows - 1) * qsn2 + 2 * D) : 0;
+        rq[3] = 0x00020000;
+        rd[0] = (int)(uint32_t)db64;
+        rd[1] = (int)((uint32_t)(db64 >> 32) & 0xffffu);
+        rd[2] = rows > 0 ? (int)((uint32_t)(rows - 1) * dsn2 + 2 * D) : 0;
+        rd[3] = 0x00020000;
+        const uint32_t piece = stage + lds_piece;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            load16_to_lds(rq, qoff[j], piece + 1024u * j);
+            load16_to_lds(rd, doff[j], piece + kLdsTileB + 1024u * j);
+        }
+        if (stat_wave)
+            load4_to_lds(rsrc_words(ld_st + r0, rows > 0 ? (uint32_t)(4 * rows) : 0u), (uint32_t)(4 * lane),
+                         stage + lds_stat);
+        // advance to the next step
+        if (++ld_j == (ld_masked ? m_per : u_per)) {
+            ld_j = 0;
+            if (++ld_gq == G) {
+                ld_gq = 0;
+                ld_masked = false;
+                ld_q = q_head0;
+                ld_d = d_head0;
+                ld_st = st_head0;
+            } else {
+                ld_q += 2 * p.qsh;
+                ld_d += 2 * p.dsh;
+                ld_st += st_dh;
+            }
+        }
+    };
+
+    // Read-ahead of the LDS operands: without the scheduling hints the compiler issues each
+    // product right behind its own reads and waits for them (lgkmcnt(0)), exposing the full
+    // LDS latency on every product. Row-read phase (S or dP): 16 products, one read each, six
+    // ahead; gradient phase (dV or dK): 16 products, two transposing reads each, ten ahead.
+    // Each product phase is fenced off (sched_barrier) so that the statistics and exchange
+    // reads of the vector phases cannot take the places the hints give its reads.
+    // Addresses: one add per column (hidden from the compiler, which would otherwise fold the
+    // row offsets into more adds), the row offsets in the instructions' immediate fields.
+    auto rows_phase_hints = [] {
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int k = 0; k < 10; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    };
+    auto grad_phase_hints = [] {
+        __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+#pragma unroll
+        for (int k = 0; k < 11; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);
+    };
+    // S (P wave) or dP (dS wave) of the stage at byte offset `so`: rows of the wave's row tile
+    // times the register K or V, accumulated onto `a`.
+    auto row_products = [&](uint32_t so, f32x16 (&a)[2]) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+        const uint32_t rb = lds0 + so + row_tile;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            uint32_t x = ar[ks] + rb;
+            asm("" : "+v"(x));
+#pragma unroll
+            for (int m = 0; m < 2; ++m) a[m] = mfma32(lds16(x + 32 * m * kLdsRowB), kv[ks], a[m]);
+        }
+        rows_phase_hints();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+    };
+    // acc += (transposed tile)^T (P or dS): 32 transposing reads, 16 products.
+    auto grad_products = [&](uint32_t so, const bf16x8 (&bop)[2][2]) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+        const uint32_t tb = lds0 + so + tr_tile;
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb) {
+            uint32_t x0 = at[cb][0] + tb, x1 = at[cb][1] + tb;
+            asm("" : "+v"(x0), "+v"(x1));
+            bf16x8 op[2][2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const uint32_t ro = (32 * m + 16 * s2) * kLdsRowB;
+                    const u32x2 lo = lds_tr4(x0 + ro);
+                    const u32x2 hi = lds_tr4(x1 + ro);
+                    u32x4 x;
+                    x[0] = lo[0]; x[1] = lo[1]; x[2] = hi[0]; x[3] = hi[1];
+                    op[m][s2] = as_bf16x8(x);
+                }
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) acc[cb] = mfma32(op[m][s2], bop[m][s2], acc[cb]);
+        }
+        grad_phase_hints();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // P wave, vector phase of the step at stage `so` with first row r0: P from S (masked in the
+    // diagonal steps), to the exchange buffer (fp16) and as bf16 B operands.
+    auto probs = [&](auto masked_c, uint32_t so, int r0, const f32x16 (&sacc)[2], bf16x8 (&pb)[2][2]) {
+        constexpr bool MASKED = decltype(masked_c)::value;
+        uint32_t sa = stat_lane + so + lds0;
+        uint32_t xa = xlane + xbuf;
+        asm("" : "+v"(sa), "+v"(xa));
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            // element r: query 32 m + 8 (r / 4) + 4 hf + r % 4 of the step (acc_row)
+            float pr[16];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 l4 = lds_f32x4(sa + 4 * (32 * m + 8 * j));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pr[4 * j + e] = fast_exp2(fmaf(sacc[m][4 * j + e], c, -l4[e]));
+            }
+            if constexpr (MASKED) {
+                // keys after their query: key - r0 - 32 m - 4 hf > 8 (r / 4) + r % 4
+                const int lim = key - r0 - 32 * m - 4 * hf;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) pr[r] = 8 * (r >> 2) + (r & 3) < lim ? 0.0f : pr[r];
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                pb[m][s2] = pack8(pr[8 * s2], pr[8 * s2 + 1], pr[8 * s2 + 2], pr[8 * s2 + 3], pr[8 * s2 + 4],
+                                  pr[8 * s2 + 5], pr[8 * s2 + 6], pr[8 * s2 + 7]);
+                f16x8 h;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) h[e] = (_Float16)pr[8 * s2 + e];
+                *(__attribute__((address_space(3))) f16x8*)(uintptr_t)(xa + (2 * m + s2) * 1024) = h;
+            }
+        }
+    };
+
+    // dS wave: dP - D of the step at stage `so` into dacc (the accumulators start at -D).
+    f32x16 dacc[2];
+    auto dp_products = [&](uint32_t so) {
+        uint32_t sa = stat_lane + so + lds0;
+        asm("" : "+v"(sa));
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 d4 = lds_f32x4(sa + 4 * (32 * m + 8 * j));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dacc[m][4 * j + e] = d4[e];
+            }
+        row_products(so, dacc);
+    };
+    // dS wave: dS = P (dP - D) with P from the exchange buffer and dP - D in dacc.
+    auto ds_values = [&](bf16x8 (&db)[2][2]) {
+        uint32_t xa = xlane + xbuf;
+        asm("" : "+v"(xa));
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const f16x8 h = *(const __attribute__((address_space(3))) f16x8*)(uintptr_t)(xa + (2 * m + s2) * 1024);
+                float ds[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ds[e] = (float)h[e] * dacc[m][8 * s2 + e];
+                db[m][s2] = pack8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+            }
+    };
+
+    if (!pwave) {
+        if (n_all > 0) issue_next(lds0);
+        if (n_all > 1) issue_next(lds0 + kPairStageB);
+    }
+    // Settle every outstanding load (the K/V rows and steps 0 and 1) before the loop.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // Iteration t (two barriers, see above). Stage of step s: s % 4; the loads of step t + 2
+    // go to the stage of step t - 2, last read by the dS waves in iteration t - 1. Each kind of
+    // wave runs its own copy of the loop (the same iterations and barriers), so that neither
+    // holds the other's registers. The P waves take the masked steps first, in a loop of their
+    // own, so that the others carry no element test.
+    int t = 0;
+    auto stage_of = [&](int s) -> uint32_t { return (uint32_t)((s & (kPairStages - 1)) * kPairStageB); };
+    if (pwave) {
+        auto iterate = [&](auto masked_c) {
+            const bool active = t < n_all;
+            f32x16 sacc[2] = {f32x16{}, f32x16{}};
+            if (active) row_products(stage_of(t), sacc);
+            __syncthreads();   // the dS waves have read the exchange buffer
+            bf16x8 pb[2][2];
+            if (active) {
+                // masked steps (the first n_mask): the diagonal block's halves, m_per per head
+                const int r0 = k0 + (m_per == 2 ? (t & 1) : 0) * kStep;
+                probs(masked_c, stage_of(t), r0, sacc, pb);
+                grad_products(stage_of(t), pb);
+            }
+            __syncthreads();
+            ++t;
+        };
+        while (t < n_mask) iterate(std::true_type{});
+        while (t <= n_all) iterate(std::false_type{});
+    } else {
+        while (t <= n_all) {
+            bf16x8 db[2][2];
+            if (t >= 1) ds_values(db);
+            const bool more = t + 2 < n_all;
+            if (more) issue_next(lds0 + stage_of(t + 2));
+            __syncthreads();   // the exchange buffer is read; the P waves may overwrite it
+            if (t >= 1) grad_products(stage_of(t - 1), db);
+            if (t < n_all) dp_products(stage_of(t));
+            // step t + 1 must have arrived; step t + 2's loads may stay in flight
+            if (more) {
+                if (stat_wave) __builtin_amdgcn_s_waitcnt(0x0F70 | 9);   // vmcnt(9)
+                else __builtin_amdgcn_s_waitcnt(0x0F70 | 8);             // vmcnt(8)
+            } else {
+                __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
+            }
+            __syncthreads();
+            ++t;
+        }
+    }
+
+    if (key < N) {
+        const float sc_out = pwave ? 1.0f : p.scale;
+        uint16_t* out = pwave ? p.dv + seq_off(sp, b, hk, p.dvsb, p.dvsh, p.dvsn) + (int64_t)key * p.dvsn
+                              : p.dk + seq_off(sp, b, hk, p.dksb, p.dksh, p.dksn) + (int64_t)key * p.dksn;
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bf16x4 a;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] = (__bf16)(acc[cb][4 * j + e] * sc_out);
+                *reinterpret_cast<bf16x4*>(out + 32 * cb + 8 * j + 4 * hf) = a;
+            }
+    }
+}
+
 // ----------------------------------------------------------------------------- dQ
 constexpr int kQ_BQ = 128;   // query rows per workgroup (32 per wave)
 
@@ -530,7 +958,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(QParams p) {
         }
     }
     const int64_t so = seq_stat_off(sp, b, hh, p.H, p.N, p.total);
-    float lse2 = 0.0f, dlt = 0.0f;
+    float lse2 = 0.0f, dlt = 0.0f;   // dlt: -D of the row
     if (qrow < N) {
         float l = p.lse[so + qrow];
         if (l == -__builtin_inff()) l = __builtin_inff();
@@ -618,7 +1046,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(QParams p) {
                         if (8 * (r >> 2) + (r & 3) > lim) dsv[r] = 0.0f;
                 }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dsv[r] *= pacc[r] - dlt;
+                for (int r = 0; r < 16; ++r) dsv[r] *= pacc[r] + dlt;   // dlt = -D
 #pragma unroll
                 for (int st = 0; st < 2; ++st)
                     db[kb][st] = pack8(dsv[8 * st], dsv[8 * st + 1], dsv[8 * st + 2], dsv[8 * st + 3],
@@ -696,7 +1124,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_dma_kernel(QParams p) {
         }
     }
     const int64_t so = seq_stat_off(sp, b, hh, p.H, p.N, p.total);
-    float lse2 = 0.0f, dlt = 0.0f;
+    float lse2 = 0.0f, dlt = 0.0f;   // dlt: -D of the row
     if (qrow < N) {
         float l = p.lse[so + qrow];
         if (l == -__builtin_inff()) l = __builtin_inff();
@@ -798,7 +1226,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_dma_kernel(QParams p) {
                         if (8 * (r >> 2) + (r & 3) > lim) dsv[r] = 0.0f;
                 }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dsv[r] *= pacc[r] - dlt;
+                for (int r = 0; r < 16; ++r) dsv[r] *= pacc[r] + dlt;   // dlt = -D
 #pragma unroll
                 for (int st = 0; st < 2; ++st)
                     db[kb][st] = pack8(dsv[8 * st], dsv[8 * st + 1], dsv[8 * st + 2], dsv[8 * st + 3],
@@ -856,7 +1284,7 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((pre_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                            static_cast<const uint16_t*>(a.o.p), packed ? 0 : a.o.sb, a.o.sh, a.o.sn,
                            static_cast<const uint16_t*>(a.dout.p), packed ? 0 : a.dout.sb, a.dout.sh, a.dout.sn,
-                           a.delta, L.H, Np, rows);
+                           a.lse, a.delta, a.delta + rows, L.H, Np, rows);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -869,6 +1297,7 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
         p.dout = static_cast<const uint16_t*>(a.dout.p);
         p.lse = a.lse;
         p.delta = a.delta;
+        p.lse2 = a.delta + (int64_t)(L.cu ? 1 : L.B) * L.H * (L.cu ? L.total : L.N);
         p.dk = static_cast<uint16_t*>(a.dk);
         p.dv = static_cast<uint16_t*>(a.dv);
         p.qsb = a.q.sb; p.qsh = a.q.sh; p.qsn = a.q.sn;
@@ -888,7 +1317,10 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
         p.c = c;
         p.scale = a.scale;
         const int64_t grid = (int64_t)L.B * L.Hkv * p.nkb;
-        hipLaunchKernelGGL((dkdv16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads16), 0, stream, p);
+        if constexpr (D == 128)
+            hipLaunchKernelGGL((dkdv_pair_kernel<CAUSAL>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+        else
+            hipLaunchKernelGGL((dkdv16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads16), 0, stream, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

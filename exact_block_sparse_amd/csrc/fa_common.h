@@ -257,6 +257,36 @@ __device__ __forceinline__ void load16_to_lds(i32x4 r, uint32_t voff, uint32_t l
                  : "memory");
 }
 
+// 4 bytes per lane from the buffer at byte offset `voff` into LDS at `lds` + 4 * lane: one
+// wave instruction fills 256 bytes (a row of 64 fp32 statistics). Same M0 contract as above.
+// The descriptor and the LDS address must be wave-uniform; they are read from the first lane
+// so that they sit in scalar registers even where the compiler cannot prove them uniform.
+__device__ __forceinline__ void load4_to_lds(i32x4 r, uint32_t voff, uint32_t lds) {
+    i32x4 u;
+    u[0] = __builtin_amdgcn_readfirstlane(r[0]);
+    u[1] = __builtin_amdgcn_readfirstlane(r[1]);
+    u[2] = __builtin_amdgcn_readfirstlane(r[2]);
+    u[3] = __builtin_amdgcn_readfirstlane(r[3]);
+    const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(u), "s"(l)
+                 : "memory");
+}
+
+// 16-byte row read and 8-byte transposing read at an LDS byte address.
+__device__ __forceinline__ bf16x8 lds16(uint32_t addr) {
+    return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)addr;
+}
+__device__ __forceinline__ u32x2 lds_tr4(uint32_t addr) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)addr));
+}
+__device__ __forceinline__ f32x4 lds_f32x4(uint32_t addr) {
+    return *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)addr;
+}
+
 // Per-thread part of one step's K and V loads: a 64-row tile is 16 pieces of 1 KB; each of
 // the NW waves loads 16 / NW consecutive pieces of K and as many of V. A stage holds the K
 // tile (swizzle SK) and then the V tile (swizzle SV). Rows past the end read as zeros (the

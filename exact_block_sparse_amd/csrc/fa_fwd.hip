@@ -567,16 +567,6 @@ struct DmaAddr {
     }
 };
 
-// 16-byte row read and 8-byte transposing read at an LDS byte address.
-__device__ __forceinline__ bf16x8 lds16(uint32_t addr) {
-    return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)addr;
-}
-__device__ __forceinline__ u32x2 lds_tr4(uint32_t addr) {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    return __builtin_bit_cast(
-        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)addr));
-}
-
 // S^T = K Q^T for one 64-key step from the swizzled stage at byte offset `so` (same products
 // as scores()).
 __device__ __forceinline__ void scores_sw(uint32_t so, Rows<128, false>& w, const DmaAddr& a) {

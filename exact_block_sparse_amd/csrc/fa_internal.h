@@ -52,7 +52,7 @@ struct BwdArgs {
     int64_t dksb, dksh, dksn;
     void* dv;
     int64_t dvsb, dvsh, dvsn;
-    float* delta;  // workspace: fp32, laid out like the LSE
+    float* delta;  // workspace: fp32 -D, laid out like the LSE, then the LSE in the exp2 domain
     Layout L;
     int causal;
     float scale;
@@ -71,7 +71,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
 // Size of the library-owned backward workspace (one per GPU).
-constexpr size_t kStaticWorkspaceBytes = (size_t)16 << 20;
+constexpr size_t kStaticWorkspaceBytes = (size_t)32 << 20;
 // Device address of the current device's library-owned workspace (set up on first use).
 hipError_t static_workspace(void** ptr);
 

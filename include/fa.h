@@ -134,8 +134,9 @@ FA_API int fa_sparse_fwd(const void* q, const void* k, const void* v, void* o, f
                   int64_t nnz, int causal, float scale, void* stream);
 
 /*
- * fa_bwd_workspace_bytes - device workspace fa_bwd needs: one fp32 per query row
- * (the row dot products D_i = dO_i . O_i), B*H*N*4 bytes rounded up to 256.
+ * fa_bwd_workspace_bytes - device workspace fa_bwd needs: two fp32 per query row (the row
+ * dot products D_i = dO_i . O_i and the row's LSE converted for base-2 exponentials),
+ * B*H*N*8 bytes rounded up to 256.
  */
 FA_API size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
 
@@ -244,8 +245,8 @@ FA_API int fa_attn_fwd(const fa_attn_desc* desc, const void* q, fa_strides sq, c
                        const void* v, fa_strides sv, void* o, fa_strides so, float* lse, void* stream);
 
 /*
- * fa_attn_bwd_workspace_bytes - device workspace fa_attn_bwd needs: one fp32 per query row
- * and query head (H * B * N, or H * total when packed) times 4 bytes, rounded up to 256.
+ * fa_attn_bwd_workspace_bytes - device workspace fa_attn_bwd needs: two fp32 per query row
+ * and query head (H * B * N, or H * total when packed) times 8 bytes, rounded up to 256.
  * 0 for an empty problem or a NULL desc.
  */
 FA_API size_t fa_attn_bwd_workspace_bytes(const fa_attn_desc* desc);
@@ -281,7 +282,7 @@ FA_API int fa_attn_bwd(const fa_attn_desc* desc, const void* q, fa_strides sq, c
  * results; serialize them, e.g. on one stream.
  * Errors as in fa_attn_bwd.
  */
-#define FA_NOALLOC_WORKSPACE_BYTES ((size_t)16 << 20)
+#define FA_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)
 FA_API int fa_attn_bwd_noalloc(const fa_attn_desc* desc, const void* q, fa_strides sq, const void* k, fa_strides sk,
                                const void* v, fa_strides sv, const void* o, fa_strides so, const void* dout,
                                fa_strides sdo, const float* lse, void* dq, fa_strides sdq, void* dk, fa_strides sdk,

@@ -93,7 +93,7 @@ def test_sparse_argument_errors(fa):
 
 
 def test_bwd_workspace_rules(fa):
-    assert fa.bwd_workspace_bytes(2, 32, 8192, 128) == 2 * 32 * 8192 * 4
+    assert fa.bwd_workspace_bytes(2, 32, 8192, 128) == 2 * 32 * 8192 * 8
     assert fa.bwd_workspace_bytes(1, 1, 3, 64) == 256
     assert fa.bwd_workspace_bytes(0, 1, 3, 64) == 0
     s = strides(8192, 8192, 128)
@@ -238,11 +238,11 @@ def test_attn_bwd_argument_errors(fa):
 def test_attn_workspace_bytes(fa):
     lib = fa.lib
     x = make_desc(fa, B=2, H=8, H_kv=2, N=1000)
-    assert lib.fa_attn_bwd_workspace_bytes(ctypes.byref(x)) == (2 * 8 * 1000 * 4 + 255) // 256 * 256
+    assert lib.fa_attn_bwd_workspace_bytes(ctypes.byref(x)) == (2 * 8 * 1000 * 8 + 255) // 256 * 256
     x = make_desc(fa, B=3, H=8, H_kv=1, N=700, cu_seqlens=16, total=1234)
-    assert lib.fa_attn_bwd_workspace_bytes(ctypes.byref(x)) == (8 * 1234 * 4 + 255) // 256 * 256
+    assert lib.fa_attn_bwd_workspace_bytes(ctypes.byref(x)) == (8 * 1234 * 8 + 255) // 256 * 256
     assert lib.fa_attn_bwd_workspace_bytes(None) == 0
-    assert fa.attn_bwd_workspace_bytes(3, 8, 700, 128, total=1234) == (8 * 1234 * 4 + 255) // 256 * 256
+    assert fa.attn_bwd_workspace_bytes(3, 8, 700, 128, total=1234) == (8 * 1234 * 8 + 255) // 256 * 256
     assert fa.attn_bwd_workspace_bytes(2, 8, 1000, 128) == fa.bwd_workspace_bytes(2, 8, 1000, 128)
 
 

@@ -65,7 +65,7 @@ def test_noalloc_packed_grouped_block_sparse(fa):
 
 
 def test_noalloc_refuses_problems_beyond_its_workspace(fa):
-    # 2 x 16 heads x 131072 rows need 16 MiB + 1 row pair over the limit: refused on the host
+    # 2 x 16 heads x 131073 rows need more than the 32 MiB (4,194,304 head-row pairs): refused on the host
     x = fa.AttnDesc()
     x.B, x.H, x.H_kv, x.N, x.d, x.causal, x.scale = 2, 16, 16, 131072 + 1, 128, 1, 0.1
     assert fa.lib.fa_attn_bwd_workspace_bytes(ctypes.byref(x)) > fa.NOALLOC_WORKSPACE_BYTES
