@@ -1184,9 +1184,35 @@ __global__ __launch_bounds__(kThreads, 2) void dq_dma_kernel(QParams p) {
     st.init(wave, lane, p.ksn, p.vsn);
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t lds0 = lds_address(smem);
+    // Loads of the key tile starting at kt0 (< N) into the stage at LDS address `stage`: the
+    // per-lane offsets of the wave's four 1-KB pieces of each tile are fixed, so per step only
+    // the tile base (a 32x32->64-bit multiply and an add per tensor) and the byte count change.
+    const uint32_t ksn2 = (uint32_t)(2 * p.ksn), vsn2 = (uint32_t)(2 * p.vsn);
+    const uint32_t piece0 = 1024u * 4u * (uint32_t)wave_u;
+    auto issue = [&](int kt0, uint32_t stage) {
+        const uint32_t rows = (uint32_t)min(N - kt0, kStep);
+        const uint64_t kb64 = reinterpret_cast<uint64_t>(kp) + (uint64_t)(uint32_t)kt0 * ksn2;
+        const uint64_t vb64 = reinterpret_cast<uint64_t>(vp) + (uint64_t)(uint32_t)kt0 * vsn2;
+        i32x4 rk, rv;
+        rk[0] = (int)(uint32_t)kb64;
+        rk[1] = (int)((uint32_t)(kb64 >> 32) & 0xffffu);
+        rk[2] = (int)((rows - 1) * ksn2 + 2 * D);
+        rk[3] = 0x00020000;
+        rv[0] = (int)(uint32_t)vb64;
+        rv[1] = (int)((uint32_t)(vb64 >> 32) & 0xffffu);
+        rv[2] = (int)((rows - 1) * vsn2 + 2 * D);
+        rv[3] = 0x00020000;
+        const uint32_t piece = stage + piece0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            load16_to_lds(rk, st.koff[j], piece + 1024u * j);
+            load16_to_lds(rv, st.voff[j], piece + kLdsTileB + 1024u * j);
+        }
+    };
+    static_assert(kThreads / 64 == 4, "four waves of four pieces per tile");
     if (nsteps > 0) {
         const int kt0 = step_key(0);
-        if (kt0 >= 0) st.issue(kp, vp, p.ksn, p.vsn, kt0, N, lds0, wave_u);
+        if (kt0 >= 0) issue(kt0, lds0);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -1195,7 +1221,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_dma_kernel(QParams p) {
         // the other stage was last read in the previous step, which ended with a barrier
         if (t + 1 < nsteps) {
             const int ktn = step_key(t + 1);
-            if (ktn >= 0) st.issue(kp, vp, p.ksn, p.vsn, ktn, N, lds0 + (cur ^ 1) * STAGEB, wave_u);
+            if (ktn >= 0) issue(ktn, lds0 + (cur ^ 1) * STAGEB);
         }
         const unsigned char* buf = smem + cur * STAGEB;
         const int kt = step_key(t);
