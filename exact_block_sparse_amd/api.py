@@ -394,7 +394,7 @@ def attn_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None =
     return dq, dk, dv
 
 
-NOALLOC_WORKSPACE_BYTES = 16 << 20   # FA_NOALLOC_WORKSPACE_BYTES of fa.h
+NOALLOC_WORKSPACE_BYTES = 32 << 20   # FA_NOALLOC_WORKSPACE_BYTES of fa.h
 
 
 def attn_bwd_noalloc(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None = None, cu_seqlens=None,
