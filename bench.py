@@ -275,7 +275,7 @@ def cpu_baseline(samples, seconds_target: float = 15.0, per_workload_seconds: fl
     import numpy as np
 
     cores = max(1, min(os.cpu_count() or 1, CPU_WORKERS_MAX))
-    rate = 0.5e9   # rough per-core fp64 rate of the row-at-a-time oracle, to size the samples
+    rate = 1.5e9   # rough per-core fp64 rate of the row-at-a-time oracle, to size the samples
     ctx = mp.get_context("fork")
     results = {}
     for key, (w, head) in samples.items():

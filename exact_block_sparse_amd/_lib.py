@@ -14,7 +14,7 @@ FA_STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 4: "FA_ERR_LAYOUT",
     5: "FA_ERR_LIST", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP", 8: "FA_ERR_ARG", 9: "FA_ERR_CAPACITY",
 }
-EXPORTS = ("fa_fwd", "fa_sparse_fwd", "fa_bwd_workspace_bytes", "fa_bwd", "fa_attn_fwd",
+EXPORTS = ("fa_fwd", "fa_sparse_fwd", "fa_bwd_workspace_bytes", "fa_bwd", "fa_attn_fwd", "fa_attn_fwd_visits",
            "fa_attn_bwd_workspace_bytes", "fa_attn_bwd", "fa_attn_bwd_noalloc", "fa_transpose_block_lists", "fa_make_block_lists",
            "fa_check_block_lists", "fa_status_str", "fa_last_error")
 
@@ -62,6 +62,8 @@ def _load() -> ctypes.CDLL:
     sz = ctypes.c_size_t
     lib.fa_attn_fwd.argtypes = [D, vp, S, vp, S, vp, S, vp, S, vp, vp]
     lib.fa_attn_fwd.restype = i32
+    lib.fa_attn_fwd_visits.argtypes = [D, vp, S, vp, S, vp, S, vp, S, vp, vp, vp]
+    lib.fa_attn_fwd_visits.restype = i32
     lib.fa_attn_bwd_workspace_bytes.argtypes = [D]
     lib.fa_attn_bwd_workspace_bytes.restype = sz
     lib.fa_attn_bwd.argtypes = [D, vp, S, vp, S, vp, S, vp, S, vp, S, vp, vp, S, vp, S, vp, S, vp, sz, vp]

@@ -323,6 +323,24 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool 
     k and v [total, H_kv, d]; returns O like q and LSE [H, total]. ``max_seqlen`` bounds every
     sequence's length (computed from host offsets when omitted).
     """
+    return _attn_fwd(q, k, v, causal, scale, cu_seqlens, max_seqlen, kv_offsets, kv_indices, block_size, out, lse,
+                     (q_descale, k_descale, v_descale), False)
+
+
+def attn_fwd_visits(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, kv_offsets, kv_indices,
+                    causal: bool = False, scale: float | None = None, cu_seqlens=None,
+                    max_seqlen: int | None = None, block_size: int = BLOCK,
+                    out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                    q_descale: float = 1.0, k_descale: float = 1.0, v_descale: float = 1.0):
+    """Block-sparse ``attn_fwd`` through ``fa_attn_fwd_visits``: returns (O, LSE, visits), where
+    visits is a uint8 tensor [B * H, nnz, 2] holding 1 at (b * H + h, e, half) for every half of
+    list entry e that sequence b, head h took into its softmax, and 0 for skipped entries."""
+    return _attn_fwd(q, k, v, causal, scale, cu_seqlens, max_seqlen, kv_offsets, kv_indices, block_size, out, lse,
+                     (q_descale, k_descale, v_descale), True)
+
+
+def _attn_fwd(q, k, v, causal, scale, cu_seqlens, max_seqlen, kv_offsets, kv_indices, block_size, out, lse,
+              descales, want_visits):
     packed = cu_seqlens is not None
     _check_group(q, k, v, packed, allow_fp8=True)
     fp8 = q.dtype != torch.bfloat16
@@ -343,7 +361,16 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool 
     _check_tensor_arg("out", o, q.shape, q.device)
     _check_stats_arg("lse", l, lshape, q.device)
     S = _packed_strides if pk else _strides
-    x = _desc(B, H, H_kv, N, d, causal, _scale(scale, d), cu, total, lists, fp8, (q_descale, k_descale, v_descale))
+    x = _desc(B, H, H_kv, N, d, causal, _scale(scale, d), cu, total, lists, fp8, descales)
+    if want_visits:
+        if lists is None:
+            raise ValueError("attn_fwd_visits needs block lists (kv_offsets, kv_indices)")
+        visits = torch.zeros((B * H, int(x.nnz), 2), dtype=torch.uint8, device=q.device)
+        with torch.cuda.device(q.device):
+            st = lib.fa_attn_fwd_visits(ctypes.byref(x), _ptr(q), S(q), _ptr(k), S(k), _ptr(v), S(v), _ptr(o), S(o),
+                                        _ptr(l), _ptr(visits), _stream(q.device))
+        check(st, "fa_attn_fwd_visits")
+        return o, l, visits
     with torch.cuda.device(q.device):
         st = lib.fa_attn_fwd(ctypes.byref(x), _ptr(q), S(q), _ptr(k), S(k), _ptr(v), S(v), _ptr(o), S(o), _ptr(l),
                              _stream(q.device))

@@ -186,15 +186,14 @@ fa_attn_desc plain_desc(int64_t B, int64_t H, int64_t N, int64_t d, int causal, 
     return x;
 }
 
-}  // namespace
-
-extern "C" {
-
-int fa_attn_fwd(const fa_attn_desc* desc, const void* q, fa_strides sq, const void* k, fa_strides sk, const void* v,
-                fa_strides sv, void* o, fa_strides so, float* lse, void* stream) {
+// The forward of fa_attn_fwd; with `visits` set (block-sparse only, checked by the caller)
+// the kernels also write the visit log, which is zero-filled first on the same stream.
+int attn_fwd(const fa_attn_desc* desc, const void* q, fa_strides sq, const void* k, fa_strides sk, const void* v,
+             fa_strides sv, void* o, fa_strides so, float* lse, uint8_t* visits, void* stream) {
     int st = check_desc(desc, false);
     if (st) return st;
     const fa_attn_desc& d = *desc;
+    if (visits && !d.kv_offsets) return fail(FA_ERR_ARG, "a visit log needs block-sparse lists (kv_offsets)");
     if (empty_problem(d)) return ok();
     const bool f8 = d.dtype == FA_DTYPE_FP8_E4M3;
     const int m = f8 ? 16 : 8;
@@ -218,7 +217,30 @@ int fa_attn_fwd(const fa_attn_desc* desc, const void* q, fa_strides sq, const vo
     a.kv_offsets = d.kv_offsets;
     a.kv_indices = d.kv_offsets ? or_other(d.kv_indices, d.kv_offsets) : nullptr;
     a.nnz = d.kv_offsets ? d.nnz : 0;
-    return launched(fa::launch_fwd(a, static_cast<hipStream_t>(stream)), "forward");
+    a.visits = nullptr;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (visits && a.nnz > 0) {
+        const size_t bytes = (size_t)d.B * (size_t)d.H * 2 * (size_t)a.nnz;
+        if (hipMemsetAsync(visits, 0, bytes, s) != hipSuccess) return launched(hipGetLastError(), "visit log fill");
+        a.visits = visits;
+    }
+    return launched(fa::launch_fwd(a, s), "forward");
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_attn_fwd(const fa_attn_desc* desc, const void* q, fa_strides sq, const void* k, fa_strides sk, const void* v,
+                fa_strides sv, void* o, fa_strides so, float* lse, void* stream) {
+    return attn_fwd(desc, q, sq, k, sk, v, sv, o, so, lse, nullptr, stream);
+}
+
+int fa_attn_fwd_visits(const fa_attn_desc* desc, const void* q, fa_strides sq, const void* k, fa_strides sk,
+                       const void* v, fa_strides sv, void* o, fa_strides so, float* lse, uint8_t* visits,
+                       void* stream) {
+    if (!visits) return fail(FA_ERR_NULL, "visits is NULL");
+    return attn_fwd(desc, q, sq, k, sk, v, sv, o, so, lse, visits, stream);
 }
 
 size_t fa_attn_bwd_workspace_bytes(const fa_attn_desc* desc) {

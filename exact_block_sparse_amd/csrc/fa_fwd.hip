@@ -84,6 +84,7 @@ struct Params {
     const int32_t* kv_offsets;
     const int32_t* kv_indices;
     int64_t nnz;
+    uint8_t* visits;  // block-sparse visit log [B * H, nnz, 2], or nullptr
 };
 
 // Per-thread staging of one K/V step: 16-byte row chunks of K and V.
@@ -709,6 +710,13 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_dma_kernel(Params 
 // ----------------------------------------------------------------------------- sparse
 constexpr int kSpThreads = 256;   // 4 waves, one 128-row block
 
+// Visit log of the block-sparse kernels (only when p.visits is set): the workgroup of
+// (sequence b, head hh) marks step tt, i.e. half (tt & 1) of list entry (tt >> 1), as taken
+// into its softmax. One lane writes one byte per step, so the log costs a store per step.
+__device__ __forceinline__ void log_visit(const Params& p, int b, int hh, int tt, int tid) {
+    if (p.visits != nullptr && tid == 0) p.visits[((int64_t)b * p.H + hh) * (2 * p.nnz) + tt] = 1;
+}
+
 template <int D, bool CAUSAL, bool F8>
 __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
     using C = Cfg<D, F8>;
@@ -774,6 +782,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
 
     int cur = 0;
     while (t < t_end) {
+        log_visit(p, b, hh, t, tid);
         int tn = t + 1, ktn = -1;
         while (tn < t_end && (ktn = step_key(tn)) < 0) ++tn;
         const bool has_next = tn < t_end;
@@ -865,6 +874,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_dma_kernel(Params p)
 
     int cur = 0;
     while (t < t_end) {
+        log_visit(p, b, hh, t, tid);
         int tn = t + 1, ktn = -1;
         while (tn < t_end && (ktn = step_key(tn)) < 0) ++tn;
         const bool has_next = tn < t_end;
@@ -952,6 +962,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     p.kv_offsets = a.kv_offsets;
     p.kv_indices = a.kv_indices;
     p.nnz = a.nnz;
+    p.visits = a.visits;
     const bool sparse = a.kv_offsets != nullptr;
     if (a.L.d == 64) return dispatch_d<64>(p, a.causal != 0, sparse, a.f8 != 0, stream);
     return dispatch_d<128>(p, a.causal != 0, sparse, a.f8 != 0, stream);

@@ -41,6 +41,9 @@ struct FwdArgs {
     const int32_t* kv_offsets;
     const int32_t* kv_indices;
     int64_t nnz;
+    // optional visit log of the block-sparse kernels: byte [(b * H + h) * 2 * nnz + 2 * e + half]
+    // is set to 1 when sequence b, head h takes half `half` of list entry e into its softmax
+    uint8_t* visits = nullptr;
 };
 
 struct BwdArgs {

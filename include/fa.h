@@ -245,6 +245,27 @@ FA_API int fa_attn_fwd(const fa_attn_desc* desc, const void* q, fa_strides sq, c
                        const void* v, fa_strides sv, void* o, fa_strides so, float* lse, void* stream);
 
 /*
+ * fa_attn_fwd_visits - fa_attn_fwd for a block-sparse desc (kv_offsets != NULL) that also
+ * records which tiles each query block took into its softmax, so that a caller can check
+ * that every query block visits exactly the key blocks its list names, less the ones the
+ * causal mask or the sequence end removes ("How Does Flash-MSA Sparse Attention Work",
+ * section "How Flash-MSA Sparse Attention Works": the kernel walks a query block's index
+ * list and nothing else; unlisted blocks are never loaded). Same outputs as fa_attn_fwd,
+ * bit for bit.
+ * visits : device uint8 [B * H, nnz, 2] (b-major: row b * H + h), written by the call: it
+ *          is zero-filled on `stream` (an asynchronous memset), then byte
+ *          [(b * H + h) * 2 * nnz + 2 * e + half] is set to 1 when sequence b, head h took
+ *          the 64 keys 128 * kv_indices[e] + 64 * half .. +63 of list entry e into the softmax
+ *          of its query block (the block whose list range holds e). Skipped entries (index
+ *          out of range, above the diagonal under causal masking, or a half past the
+ *          sequence end or past the query block's last row) stay 0.
+ * Errors as in fa_attn_fwd; FA_ERR_NULL for visits == NULL; FA_ERR_ARG for a dense desc.
+ */
+FA_API int fa_attn_fwd_visits(const fa_attn_desc* desc, const void* q, fa_strides sq, const void* k,
+                              fa_strides sk, const void* v, fa_strides sv, void* o, fa_strides so, float* lse,
+                              uint8_t* visits, void* stream);
+
+/*
  * fa_attn_bwd_workspace_bytes - device workspace fa_attn_bwd needs: two fp32 per query row
  * and query head (H * B * N, or H * total when packed) times 8 bytes, rounded up to 256.
  * 0 for an empty problem or a NULL desc.

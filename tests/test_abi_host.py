@@ -220,6 +220,23 @@ def test_attn_fwd_argument_errors(fa):
     assert call_attn_fwd(fa, make_desc(fa, cu_seqlens=16, total=0), q=0) == 0
 
 
+def call_attn_fwd_visits(fa, desc, visits=16):
+    s = strides(8192, 8192, 128)
+    p = ctypes.c_void_p(16)
+    d = ctypes.byref(desc) if desc is not None else None
+    return fa.lib.fa_attn_fwd_visits(d, p, s, p, s, p, s, p, s, p, ctypes.c_void_p(visits), None)
+
+
+def test_attn_fwd_visits_argument_errors(fa):
+    sparse = dict(kv_offsets=16, kv_indices=16, block_size=128, nnz=4)
+    assert call_attn_fwd_visits(fa, make_desc(fa, **sparse), visits=0) == 1    # NULL log
+    assert "visits" in fa.lib.fa_last_error().decode()
+    assert call_attn_fwd_visits(fa, make_desc(fa)) == 8                        # dense: nothing to log
+    assert "kv_offsets" in fa.lib.fa_last_error().decode()
+    assert call_attn_fwd_visits(fa, None) == 1
+    assert call_attn_fwd_visits(fa, make_desc(fa, B=0, **sparse)) == 0          # empty: nothing launched
+
+
 def test_attn_bwd_argument_errors(fa):
     assert call_attn_bwd(fa, None) == 1
     assert call_attn_bwd(fa, make_desc(fa, H=6, H_kv=4)) == 2
