@@ -118,7 +118,13 @@ def len_off(w) -> int:
 
 
 class Timer:
-    """HIP events on torch's current stream, where the library launches its kernels."""
+    """HIP events on torch's current stream, where the library launches its kernels.
+
+    The timed calls run back to back between two events (the mean per call is their
+    distance over the number of calls), so the host's work for one call overlaps the GPU's
+    work for the previous one, as in a stream of calls. A second pass with an event pair
+    around every call gives the per-call median and minimum (there each call also waits
+    for its own host-side preparation, which matters only for the smallest problems)."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -128,18 +134,25 @@ class Timer:
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
+        first, last = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        first.record()
+        for _ in range(steps):
+            fn()
+        last.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        total = first.elapsed_time(last)
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        t0 = time.perf_counter()
         for i in range(steps):
             starts[i].record()
             fn()
             ends[i].record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
         per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-        return dict(mean_ms=sum(per) / len(per), median_ms=per[len(per) // 2], min_ms=per[0],
-                    total_ms=sum(per), wall_s=wall, reps=steps)
+        return dict(mean_ms=total / steps, median_ms=per[len(per) // 2], min_ms=per[0], total_ms=total,
+                    wall_s=wall, reps=steps)
 
 
 def prepare(fa, W, torch, key):
