@@ -155,7 +155,7 @@ class Timer:
                     wall_s=wall, reps=steps)
 
 
-def prepare(fa, W, torch, key):
+def prepare(fa, W, torch, key, store_ds=None):
     w = W.WORKLOADS[key]
     log(f"[bench] preparing {key}: {w.describe()}")
     x = W.make_inputs(w)
@@ -183,7 +183,8 @@ def prepare(fa, W, torch, key):
         lists = dict(kv_offsets=torch.from_numpy(off).to("cuda"), kv_indices=torch.from_numpy(idx).to("cuda"))
         tlists = dict(q_offsets=torch.from_numpy(t_off).to("cuda"), q_indices=torch.from_numpy(t_idx).to("cuda"))
         o, lse = fa.attn_fwd(dev["q"], dev["k"], dev["v"], **kw, **lists)
-        info["fn"] = lambda: fa.attn_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], **kw, **lists, **tlists)
+        info["fn"] = lambda: fa.attn_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], **kw, **lists, **tlists,
+                                         store_ds=store_ds)
         fl, fl_exact = sparse_flops(w, off, idx)
         info["flops"], info["flops_exact"] = 2.5 * fl, 2.5 * fl_exact
         info["tiles_per_head"] = int(off[-1])
@@ -201,13 +202,13 @@ def prepare(fa, W, torch, key):
         info["bytes"] = algorithmic_bytes(w, "sparse_fwd", len(idx))
     elif general:
         o, lse = fa.attn_fwd(dev["q"], dev["k"], dev["v"], **kw)
-        info["fn"] = lambda: fa.attn_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], **kw)
+        info["fn"] = lambda: fa.attn_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], **kw, store_ds=store_ds)
         info["flops"] = 2.5 * fwd_flops(w)
         info["bytes"] = algorithmic_bytes(w, "bwd")
     else:
         o, lse = fa.fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale)
         info["fn"] = lambda: fa.bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], causal=w.causal,
-                                    scale=w.scale)
+                                    scale=w.scale, store_ds=store_ds)
         info["flops"] = 2.5 * fwd_flops(w)
         info["bytes"] = algorithmic_bytes(w, "bwd")
     return info
@@ -338,6 +339,9 @@ def main():
     ap.add_argument("--workloads", default="all",
                     help="all, headline, or a comma-separated list of workload keys (besides the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bwd-schedule", choices=("auto", "stored", "recomputed"), default="auto",
+                    help="backward: dS stored by the dK/dV pass for dQ (stored), dQ recomputing S and dP "
+                         "(recomputed), or the library binding's default choice (auto)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (to scale "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -390,7 +394,7 @@ def main():
             if key == HEADLINE:
                 others[key] = hs
                 continue
-            info = prepare(fa, W, torch, key)
+            info = prepare(fa, W, torch, key, {"auto": None, "stored": True, "recomputed": False}[args.bwd_schedule])
             if want_cpu and key in W.BENCHMARK_CONFIGS:
                 cpu_samples[key] = (info["workload"], cpu_head(info["workload"], info["x"]))
             reps = 50 if key == "dense_n512_d64" else max(20, args.steps)
@@ -437,6 +441,7 @@ def main():
                                                           2) if clock else None)},
         "cpu_baseline": cpu,
         "workloads": others,
+        "bwd_schedule": args.bwd_schedule,
         "context": "pages' claim: FlashAttention-2 2-4x faster than cuDNN attention on one A100 beyond 8K "
                    "tokens (context only, other hardware)",
     }

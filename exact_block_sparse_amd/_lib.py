@@ -14,8 +14,9 @@ FA_STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 4: "FA_ERR_LAYOUT",
     5: "FA_ERR_LIST", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP", 8: "FA_ERR_ARG", 9: "FA_ERR_CAPACITY",
 }
-EXPORTS = ("fa_fwd", "fa_sparse_fwd", "fa_bwd_workspace_bytes", "fa_bwd", "fa_attn_fwd", "fa_attn_fwd_visits",
-           "fa_attn_bwd_workspace_bytes", "fa_attn_bwd", "fa_attn_bwd_noalloc", "fa_transpose_block_lists", "fa_make_block_lists",
+EXPORTS = ("fa_fwd", "fa_sparse_fwd", "fa_bwd_workspace_bytes", "fa_bwd_ds_workspace_bytes", "fa_bwd", "fa_attn_fwd",
+           "fa_attn_fwd_visits", "fa_attn_bwd_workspace_bytes", "fa_attn_bwd_ds_workspace_bytes", "fa_attn_bwd",
+           "fa_attn_bwd_noalloc", "fa_transpose_block_lists", "fa_make_block_lists",
            "fa_check_block_lists", "fa_status_str", "fa_last_error")
 
 
@@ -55,6 +56,8 @@ def _load() -> ctypes.CDLL:
     lib.fa_sparse_fwd.restype = i32
     lib.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd_ds_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
+    lib.fa_bwd_ds_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                            S, S, S, S, S, S, S, S, i32, f32, vp, ctypes.c_size_t, vp]
     lib.fa_bwd.restype = i32
@@ -66,6 +69,8 @@ def _load() -> ctypes.CDLL:
     lib.fa_attn_fwd_visits.restype = i32
     lib.fa_attn_bwd_workspace_bytes.argtypes = [D]
     lib.fa_attn_bwd_workspace_bytes.restype = sz
+    lib.fa_attn_bwd_ds_workspace_bytes.argtypes = [D]
+    lib.fa_attn_bwd_ds_workspace_bytes.restype = sz
     lib.fa_attn_bwd.argtypes = [D, vp, S, vp, S, vp, S, vp, S, vp, S, vp, vp, S, vp, S, vp, S, vp, sz, vp]
     lib.fa_attn_bwd.restype = i32
     lib.fa_attn_bwd_noalloc.argtypes = [D, vp, S, vp, S, vp, S, vp, S, vp, S, vp, vp, S, vp, S, vp, S, vp]

@@ -77,6 +77,20 @@ def _workspace(ws, need: int, device) -> tuple[torch.Tensor, int]:
     return ws, ws.numel() * ws.element_size()
 
 
+def _bwd_workspace(ws, need: int, need_ds: int, store_ds, device) -> tuple[torch.Tensor, int]:
+    """Workspace of a backward call. A caller's tensor is used as given (its size selects the
+    schedule in the library). Otherwise store_ds=True asks for the stored-dS schedule (an
+    error where it does not exist), False for recomputation, and None takes the stored-dS
+    schedule when it exists and its workspace is at most a quarter of the device's memory."""
+    if ws is not None:
+        return _workspace(ws, need, device)
+    if store_ds and not need_ds:
+        raise ValueError("the stored-dS backward needs head dimension 128, bf16 and a non-empty problem")
+    if store_ds is None:
+        store_ds = 0 < need_ds <= torch.cuda.get_device_properties(device).total_memory // 4
+    return _workspace(None, need_ds if store_ds else need, device)
+
+
 def _empty_like_layout(t: torch.Tensor, dtype=None) -> torch.Tensor:
     """An uninitialised tensor with t's shape and, if t is a permuted dense tensor, its layout."""
     dtype = t.dtype if dtype is None else dtype
@@ -163,13 +177,21 @@ def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
     return int(lib.fa_bwd_workspace_bytes(B, H, N, d))
 
 
-def bwd(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None = None, workspace=None):
-    """Backward through ``fa_bwd``; returns (dQ, dK, dV) bf16 in the layouts of q, k, v."""
+def bwd_ds_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool = False) -> int:
+    """Workspace with which ``fa_bwd`` stores dS instead of recomputing it (0: no such schedule)."""
+    return int(lib.fa_bwd_ds_workspace_bytes(B, H, N, d, int(bool(causal))))
+
+
+def bwd(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None = None, workspace=None,
+        store_ds: bool | None = None):
+    """Backward through ``fa_bwd``; returns (dQ, dK, dV) bf16 in the layouts of q, k, v.
+    ``store_ds`` picks the schedule when no workspace is given (see ``_bwd_workspace``)."""
     _check_inputs(q, k, v, o, do)
     B, H, N, d = q.shape
     _check_stats_arg("lse", lse, (B, H, N), q.device)
     dq, dk, dv = _empty_like_layout(q), _empty_like_layout(k), _empty_like_layout(v)
-    ws, ws_bytes = _workspace(workspace, bwd_workspace_bytes(B, H, N, d), q.device)
+    ws, ws_bytes = _bwd_workspace(workspace, bwd_workspace_bytes(B, H, N, d),
+                                  bwd_ds_workspace_bytes(B, H, N, d, causal), store_ds, q.device)
     with torch.cuda.device(q.device):
         st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                         B, H, N, d, _strides(q), _strides(k), _strides(v), _strides(o), _strides(do),
@@ -386,13 +408,30 @@ def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int, total: int | None =
     return int(lib.fa_attn_bwd_workspace_bytes(ctypes.byref(x)))
 
 
+def attn_bwd_ds_workspace_bytes(B: int, H: int, N: int, d: int, *, causal: bool = False, total: int | None = None,
+                                nnz: int | None = None) -> int:
+    """Workspace with which ``fa_attn_bwd`` stores dS (``nnz``: block-sparse with that many
+    list entries; ``total``: packed rows). 0 where that schedule does not exist."""
+    x = _desc(B, H, H, N, d, causal, 1.0)
+    if total is not None:
+        x.cu_seqlens = 1   # any non-NULL value selects the packed layout; it is not read
+        x.total = int(total)
+    if nnz is not None:
+        x.kv_offsets = 1   # likewise selects block-sparse mode
+        x.block_size, x.nnz = BLOCK, int(nnz)
+    return int(lib.fa_attn_bwd_ds_workspace_bytes(ctypes.byref(x)))
+
+
 def attn_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None = None, cu_seqlens=None,
              max_seqlen: int | None = None, kv_offsets=None, kv_indices=None, q_offsets=None, q_indices=None,
-             block_size: int = BLOCK, workspace=None):
+             block_size: int = BLOCK, workspace=None, store_ds: bool | None = None):
     """General backward through ``fa_attn_bwd``; returns (dQ like q, dK like k, dV like v).
 
     Arguments as in ``attn_fwd``; ``o`` and ``lse`` are its outputs. With host block lists
     the key-side lists are derived with ``transpose_block_lists`` when not given.
+    ``store_ds`` picks the schedule when no workspace is given: True stores dS in the
+    workspace (head dimension 128), False recomputes it in the dQ pass, None (default) stores
+    it when that workspace is at most a quarter of the device's memory.
     """
     packed = cu_seqlens is not None
     _check_group(q, k, v, packed)
@@ -412,7 +451,8 @@ def attn_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None =
         dq, dk, dv = _empty_like_layout(q), _empty_like_layout(k), _empty_like_layout(v)
     S = _packed_strides if pk else _strides
     x = _desc(B, H, H_kv, N, d, causal, _scale(scale, d), cu, total, lists)
-    ws, ws_bytes = _workspace(workspace, int(lib.fa_attn_bwd_workspace_bytes(ctypes.byref(x))), q.device)
+    ws, ws_bytes = _bwd_workspace(workspace, int(lib.fa_attn_bwd_workspace_bytes(ctypes.byref(x))),
+                                  int(lib.fa_attn_bwd_ds_workspace_bytes(ctypes.byref(x))), store_ds, q.device)
     with torch.cuda.device(q.device):
         st = lib.fa_attn_bwd(ctypes.byref(x), _ptr(q), S(q), _ptr(k), S(k), _ptr(v), S(v), _ptr(o), S(o), _ptr(do),
                              S(do), _ptr(lse), _ptr(dq), S(dq), _ptr(dk), S(dk), _ptr(dv), S(dv), _ptr(ws),

@@ -251,10 +251,24 @@ size_t fa_attn_bwd_workspace_bytes(const fa_attn_desc* desc) {
     return (bytes + 255) & ~(size_t)255;
 }
 
-int fa_attn_bwd(const fa_attn_desc* desc, const void* q, fa_strides sq, const void* k, fa_strides sk, const void* v,
-                fa_strides sv, const void* o, fa_strides so, const void* dout, fa_strides sdo, const float* lse,
-                void* dq, fa_strides sdq, void* dk, fa_strides sdk, void* dv, fa_strides sdv, void* workspace,
-                size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// dS tiles of the stored-dS backward per (sequence, query head); 0 when the mode does not apply.
+int64_t ds_tiles(const fa_attn_desc& d) {
+    if (d.d != 128) return 0;
+    const int64_t nqb = (d.N + 127) / 128;
+    if (d.kv_offsets) return d.nnz > 0 ? d.nnz : 0;
+    return d.causal ? nqb * (nqb + 1) / 2 : nqb * nqb;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int attn_bwd(const fa_attn_desc* desc, const void* q, fa_strides sq, const void* k, fa_strides sk, const void* v,
+             fa_strides sv, const void* o, fa_strides so, const void* dout, fa_strides sdo, const float* lse,
+             void* dq, fa_strides sdq, void* dk, fa_strides sdk, void* dv, fa_strides sdv, void* workspace,
+             size_t workspace_bytes, bool allow_ds, void* stream) {
     int st = check_desc(desc, true);
     if (st) return st;
     const fa_attn_desc& d = *desc;
@@ -286,7 +300,41 @@ int fa_attn_bwd(const fa_attn_desc* desc, const void* q, fa_strides sq, const vo
     a.q_offsets = sparse ? d.q_offsets : nullptr;
     a.q_indices = sparse ? or_other(d.q_indices, d.q_offsets) : nullptr;
     a.nnz = sparse ? d.nnz : 0;
+    const size_t need_ds = allow_ds ? fa_attn_bwd_ds_workspace_bytes(desc) : 0;
+    if (need_ds && workspace_bytes >= need_ds) {
+        unsigned char* w = static_cast<unsigned char*>(workspace) + need;
+        if (sparse) {
+            a.ds_pos = reinterpret_cast<int32_t*>(w);
+            w += round256((size_t)d.nnz * sizeof(int32_t));
+        }
+        a.ds = reinterpret_cast<uint16_t*>(w);
+        a.ds_bh = ds_tiles(d) * 128 * 128;
+    }
     return launched(fa::launch_bwd(a, static_cast<hipStream_t>(stream)), "backward");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_attn_bwd_ds_workspace_bytes(const fa_attn_desc* desc) {
+    const size_t base = fa_attn_bwd_workspace_bytes(desc);
+    if (!base || desc->dtype != FA_DTYPE_BF16) return 0;
+    const int64_t tiles = ds_tiles(*desc);
+    if (tiles <= 0) return 0;
+    // B * H * tiles * 32 KB, refused (0) beyond 2^56 bytes
+    const double est = (double)desc->B * (double)desc->H * (double)tiles * 32768.0;
+    if (est > 7.2e16) return 0;
+    const size_t pos = desc->kv_offsets ? round256((size_t)desc->nnz * sizeof(int32_t)) : 0;
+    return base + pos + (size_t)desc->B * (size_t)desc->H * (size_t)tiles * 32768u;
+}
+
+int fa_attn_bwd(const fa_attn_desc* desc, const void* q, fa_strides sq, const void* k, fa_strides sk, const void* v,
+                fa_strides sv, const void* o, fa_strides so, const void* dout, fa_strides sdo, const float* lse,
+                void* dq, fa_strides sdq, void* dk, fa_strides sdk, void* dv, fa_strides sdv, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    return attn_bwd(desc, q, sq, k, sk, v, sv, o, so, dout, sdo, lse, dq, sdq, dk, sdk, dv, sdv, workspace,
+                    workspace_bytes, true, stream);
 }
 
 static_assert(FA_NOALLOC_WORKSPACE_BYTES == fa::kStaticWorkspaceBytes, "header and library disagree");
@@ -307,8 +355,8 @@ int fa_attn_bwd_noalloc(const fa_attn_desc* desc, const void* q, fa_strides sq, 
     void* ws = nullptr;
     const hipError_t e = fa::static_workspace(&ws);
     if (e != hipSuccess) return fail(FA_ERR_HIP, "library-owned workspace unavailable: %s", hipGetErrorString(e));
-    return fa_attn_bwd(desc, q, sq, k, sk, v, sv, o, so, dout, sdo, lse, dq, sdq, dk, sdk, dv, sdv, ws,
-                       fa::kStaticWorkspaceBytes, stream);
+    return attn_bwd(desc, q, sq, k, sk, v, sv, o, so, dout, sdo, lse, dq, sdq, dk, sdk, dv, sdv, ws,
+                    fa::kStaticWorkspaceBytes, false, stream);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
@@ -339,6 +387,11 @@ int fa_sparse_fwd(const void* q, const void* k, const void* v, void* o, float* l
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
     const fa_attn_desc x = plain_desc(B, H, N, d, 0, 1.0f);
     return fa_attn_bwd_workspace_bytes(&x);
+}
+
+size_t fa_bwd_ds_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int causal) {
+    const fa_attn_desc x = plain_desc(B, H, N, d, causal, 1.0f);
+    return fa_attn_bwd_ds_workspace_bytes(&x);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,

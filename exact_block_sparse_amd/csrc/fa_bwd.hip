@@ -148,6 +148,12 @@ struct KVParams {
     int64_t nnz;
     float c;       // scale * log2(e)
     float scale;
+    // Stored dS (dkdv_pair_kernel only; nullptr: not stored). Region of sequence b, query head
+    // h: ds + (b * H + h) * ds_bh, a run of [128 keys, 128 query positions] bf16 tiles, one per
+    // (key block, query block) pair the pass visits (numbering in dq_ds_kernel).
+    uint16_t* ds;
+    int64_t ds_bh;
+    int nqbt;      // query blocks of the tile numbering: ceil(N / 128)
 };
 
 template <int D>
@@ -820,6 +826,61 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(KVParams p) {
             }
     };
 
+    // dS wave, stored-dS mode: the step's dS as rounded for the dK product, to its tile, in
+    // register-fragment order: [query half][key group grp][m][s2][lane][8 values], so that each
+    // store instruction writes 1 KB of whole cache lines. Lane (hf, i) holds key 32 grp + i and,
+    // per (m, s2), the 8 queries 32 m + 16 s2 + 4 hf + {0..3, 8..11} of the 64-query step (the
+    // dQ pass gathers them back into rows). Keys past the sequence end store zeros (their P is
+    // not masked and is finite only for bounded LSE). The steps are walked like the loads, one
+    // behind the products; the stores are issued after the iteration's load wait, so that they
+    // complete during the next iteration.
+    int sv_gq = 0, sv_j = 0;
+    bool sv_masked = m_per > 0;
+    const bool tail_block = k0 + kKV_BK > N;   // uniform: some of the block's keys are past the end
+    const bool key_out = key >= N;
+    auto store_ds = [&](bf16x8 (&db)[2][2]) {
+        int64_t tile;
+        int half;
+        if (!steps.sparse) {
+            const int s = steps.t0 + (sv_masked ? sv_j : m_per + sv_j);   // the step's 64-row index
+            const int qb = s >> 1;
+            half = s & 1;
+            tile = CAUSAL ? (int64_t)kblk * p.nqbt - (int64_t)kblk * (kblk - 1) / 2 + (qb - kblk)
+                          : (int64_t)kblk * p.nqbt + qb;
+        } else {
+            int e = sv_j >> 1;   // list entry (from lo), as in KvSteps::row
+            if (sv_masked) e = steps.diag;
+            else if (m_per && e >= steps.diag) ++e;
+            tile = steps.lo + e;
+            half = sv_j & 1;
+        }
+        uint16_t* dst = p.ds + ((int64_t)b * p.H + (h0 + sv_gq)) * p.ds_bh + tile * (kKV_BK * 128) +
+                        half * 8192 + grp * 2048 + lane * 8;
+        if (tail_block) {
+            asm volatile("");   // a branch, not selects on every step: only the last key block has such keys
+            if (key_out) {
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) db[m][s2] = bf16x8{};
+            }
+        }
+        // written once and read once by the dQ pass: non-temporal stores, whole lines
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+                __builtin_nontemporal_store(__builtin_bit_cast(u32x4, db[m][s2]),
+                                            reinterpret_cast<u32x4*>(dst + 512 * (2 * m + s2)));
+        if (++sv_j == (sv_masked ? m_per : u_per)) {
+            sv_j = 0;
+            if (++sv_gq == G) {
+                sv_gq = 0;
+                sv_masked = false;
+            }
+        }
+    };
+
     if (!pwave) {
         if (n_all > 0) issue_next(lds0);
         if (n_all > 1) issue_next(lds0 + kPairStageB);
@@ -856,6 +917,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(KVParams p) {
         while (t <= n_all) {
             bf16x8 db[2][2];
             if (t >= 1) ds_values(db);
+            // stores before the loads: the waits below then leave only step t + 2's loads in
+            // flight and cover these stores too
             const bool more = t + 2 < n_all;
             if (more) issue_next(lds0 + stage_of(t + 2));
             __syncthreads();   // the exchange buffer is read; the P waves may overwrite it
@@ -868,6 +931,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(KVParams p) {
             } else {
                 __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
             }
+            if (t >= 1 && p.ds != nullptr) store_ds(db);
             __syncthreads();
             ++t;
         }
@@ -1294,6 +1358,249 @@ __global__ __launch_bounds__(kThreads, 2) void dq_dma_kernel(QParams p) {
 }
 
 
+// ----------------------------------------------------------------------------- dQ from stored dS
+// With a large enough workspace the dK/dV kernel stores the bf16 dS of every (key block,
+// query block) pair it visits, and dQ = scale * dS K is one product per step instead of the
+// three of dq_dma_kernel (S and dP recomputed): the rows of the tile are read back rather
+// than recomputed. Tile numbering within the region of one (sequence, query head), nqb =
+// ceil(N / 128) with N the longest sequence: dense non-causal kb * nqb + qb; dense causal
+// (qb >= kb) kb * nqb - kb (kb - 1) / 2 + qb - kb; block-sparse: the pair's entry index in the
+// key-side lists (the dQ pass finds it through `pos`, written by ds_pos_kernel).
+struct DsQParams {
+    const uint16_t* k;
+    const uint16_t* ds;
+    const int32_t* pos;          // block-sparse: key-side entry of every query-side entry, or -1
+    uint16_t* dq;
+    int64_t ksb, ksh, ksn, dqsb, dqsh, dqsn;
+    int64_t ds_bh;
+    int B, H, N, nqb, G;
+    const int32_t* cu;
+    int64_t total;
+    const int32_t* kv_offsets;   // query-side block lists (block-sparse mode), or nullptr
+    const int32_t* kv_indices;
+    int64_t nnz;
+    float scale;
+};
+
+// For every query-side entry e (query block qb, key block kv_indices[e]) the index of qb in
+// the key block's ascending key-side list, or -1 when it is not there (or the entry is out of
+// range). One wave per query block, one lane per entry (a binary search each); offsets are
+// clamped, so any list content stays in bounds.
+__global__ __launch_bounds__(256) void ds_pos_kernel(const int32_t* kv_off, const int32_t* kv_idx,
+                                                     const int32_t* q_off, const int32_t* q_idx, int64_t nnz,
+                                                     int nb, int32_t* pos) {
+    const int qb = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (qb >= nb) return;
+    auto clampo = [&](int64_t x) -> int64_t { return x < 0 ? 0 : (x > nnz ? nnz : x); };
+    const int64_t lo = clampo(kv_off[qb]);
+    int64_t hi = clampo(kv_off[qb + 1]);
+    if (hi < lo) hi = lo;
+    for (int64_t e = lo + (threadIdx.x & 63); e < hi; e += 64) {
+        const int kb = kv_idx[e];
+        int32_t r = -1;
+        if (kb >= 0 && kb < nb) {
+            const int64_t a0 = clampo(q_off[kb]);
+            int64_t z = clampo(q_off[kb + 1]);
+            if (z < a0) z = a0;
+            const int64_t end = z;
+            int64_t a = a0;
+            while (a < z) {   // first entry not below qb
+                const int64_t m = (a + z) >> 1;
+                if (q_idx[m] < qb) a = m + 1;
+                else z = m;
+            }
+            if (a < end && q_idx[a] == qb) r = (int32_t)a;
+        }
+        pos[e] = r;
+    }
+}
+
+// Lane i of a wave's 32 query positions holds query i with bits 2 and 3 swapped (the order
+// the dK/dV kernel stores a step's queries in).
+__device__ __forceinline__ int swap23(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+// dQ^T += K^T dS^T per 64-key step: the K rows and the dS rows of the same keys are loaded
+// straight into LDS (two 32 KB stages, two workgroups per CU) in the layout of dq_dma_kernel's
+// K tile, and both operands come from transposing reads of them: K^T per 32-column block of the
+// head dimension (the same for every wave), dS^T for the wave's 32 query positions. A dS row
+// (one key, 128 query positions; position p of a 64-query half holds query p with bits 2 and
+// 3 swapped) is gathered from the stored fragments: 16 bytes per 8 positions, 64 contiguous
+// bytes per 4 consecutive keys. Entries the lists or the causal mask exclude are skipped; the
+// stored dS of masked elements and of keys past the sequence end are zeros, so no element
+// needs a mask here.
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void dq_ds_kernel(DsQParams p) {
+    constexpr int D = 128, CB = D / 32;
+    constexpr int STAGEB = 2 * kLdsTileB;   // K rows | dS rows (128 query positions) of 64 keys
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGEB];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, i = lane & 31;
+    const int logical = p.kv_offsets ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = logical / p.nqb;
+    int qb = logical % p.nqb;
+    if (CAUSAL) qb = p.nqb - 1 - qb;
+    const int hh = bh / p.B, b = bh % p.B;
+    const SeqSpan sp = seq_span(p.cu, p.total, b, p.N);
+    const int N = sp.len;
+    const int q0 = qb * kQ_BQ;
+    if (q0 >= N) return;   // past the end of a shorter packed sequence (uniform per workgroup)
+
+    const int hk = hh / p.G;
+    const uint16_t* kp = p.k + seq_off(sp, b, hk, p.ksb, p.ksh, p.ksn);
+    const uint16_t* dsp = p.ds + ((int64_t)b * p.H + hh) * p.ds_bh;
+    const int qw0 = q0 + 32 * wave;
+    const int qlast = min(q0 + kQ_BQ - 1, N - 1);
+
+    int nsteps = (N + kStep - 1) / kStep;
+    if (CAUSAL) nsteps = min(nsteps, qlast / kStep + 1);
+    const bool sparse = p.kv_offsets != nullptr;
+    int64_t lo = 0;
+    if (sparse) {
+        int64_t hi = load_uniform(p.kv_offsets, qb + 1);
+        lo = load_uniform(p.kv_offsets, qb);
+        lo = lo < 0 ? 0 : (lo > p.nnz ? p.nnz : lo);
+        hi = hi < lo ? lo : (hi > p.nnz ? p.nnz : hi);
+        nsteps = (int)(2 * (hi - lo));
+    }
+    const int nkb = (N + kQ_BQ - 1) / kQ_BQ;
+    // first key of step t (-1: skipped) and the element offset of its key half of the tile
+    auto step_src = [&](int t, int64_t& src) -> int {
+        if (!sparse) {
+            const int kb = t >> 1;
+            const int64_t tile = CAUSAL ? (int64_t)kb * p.nqb - (int64_t)kb * (kb - 1) / 2 + (qb - kb)
+                                        : (int64_t)kb * p.nqb + qb;
+            src = tile * (kQ_BQ * 128) + (t & 1) * 4096;
+            return t * kStep;
+        }
+        const int64_t e = lo + (t >> 1);
+        const int kb = load_uniform(p.kv_indices, e);
+        const int ps = load_uniform(p.pos, e);
+        if (kb < 0 || kb >= nkb || (CAUSAL && kb > qb) || ps < 0 || ps >= p.nnz) return -1;
+        const int kt0 = kb * kQ_BQ + (t & 1) * kStep;
+        if (kt0 >= N || (CAUSAL && kt0 > qlast)) return -1;
+        src = (int64_t)ps * (kQ_BQ * 128) + (t & 1) * 4096;
+        return kt0;
+    };
+
+    // transposing-read offsets within a tile: per 32-column block cb (K^T) and for the wave's
+    // query positions (dS^T), for the lane's row and the row 8 below it
+    uint32_t at[CB][2], bt[2];
+    {
+        const int g16 = (lane >> 4) & 1, j16 = lane & 15;
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+            const int row = 4 * hf + (j16 >> 2) + 8 * h8;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const int chunk = 4 * cb + 2 * g16 + ((j16 & 3) >> 1);
+                at[cb][h8] = (uint32_t)(row * kLdsRowB + 16 * (chunk ^ swz<kSwzBoth>(row)) + 8 * (j16 & 1));
+            }
+            const int chunk = 4 * wave + 2 * g16 + ((j16 & 3) >> 1);
+            bt[h8] = (uint32_t)(kLdsTileB + row * kLdsRowB + 16 * (chunk ^ swz<kSwzBoth>(row)) + 8 * (j16 & 1));
+        }
+    }
+
+    DmaStage<kThreads / 64, kSwzBoth, kSwzBoth> st;
+    st.init(wave, lane, p.ksn, 128);
+    // byte offset (from the step's key half of the tile) of the fragment that fills LDS row r,
+    // physical chunk c: logical chunk c ^ swizzle = 8 positions of query half h, slot 4 m + 2 s2
+    // + hf; key group r / 32 of the half, lane 32 hf + r % 32
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 4 * (4 * wave + j) + (lane >> 4);
+        const int lc = (lane & 15) ^ swz<kSwzBoth>(r);
+        const int h = lc >> 3, slot = lc & 7;
+        const int m = slot >> 2, s2 = (slot >> 1) & 1, f = slot & 1;
+        st.voff[j] = (uint32_t)(2 * (h * 8192 + (r >> 5) * 2048 + (2 * m + s2) * 512 + (32 * f + (r & 31)) * 8));
+    }
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds0 = lds_address(smem);
+    const uint32_t ksn2 = (uint32_t)(2 * p.ksn);
+    const uint32_t piece0 = 1024u * 4u * (uint32_t)wave_u;
+    auto issue = [&](int kt0, int64_t src, uint32_t stage) {
+        const uint32_t rows = (uint32_t)min(N - kt0, kStep);
+        const uint64_t kb64 = reinterpret_cast<uint64_t>(kp) + (uint64_t)(uint32_t)kt0 * ksn2;
+        const uint64_t db64 = reinterpret_cast<uint64_t>(dsp + src);
+        i32x4 rk, rd;
+        rk[0] = (int)(uint32_t)kb64;
+        rk[1] = (int)((uint32_t)(kb64 >> 32) & 0xffffu);
+        rk[2] = (int)((rows - 1) * ksn2 + 2 * D);
+        rk[3] = 0x00020000;
+        rd[0] = (int)(uint32_t)db64;
+        rd[1] = (int)((uint32_t)(db64 >> 32) & 0xffffu);
+        rd[2] = (int)(2 * (kQ_BQ * 128 - (src & 4096)));   // to the end of the tile
+        rd[3] = 0x00020000;
+        const uint32_t piece = stage + piece0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            load16_to_lds(rk, st.koff[j], piece + 1024u * j);
+            load16_to_lds(rd, st.voff[j], piece + kLdsTileB + 1024u * j);
+        }
+    };
+    static_assert(kThreads / 64 == 4, "four waves of four pieces per tile");
+
+    f32x16 dq[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) dq[cb] = f32x16{};
+
+    int64_t src_next = 0;
+    int kt_next = nsteps > 0 ? step_src(0, src_next) : -1;
+    if (kt_next >= 0) issue(kt_next, src_next, lds0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int cur = 0;
+    for (int t = 0; t < nsteps; ++t) {
+        const int kt = kt_next;
+        // the other stage was last read in the previous step, which ended with a barrier
+        if (t + 1 < nsteps) {
+            kt_next = step_src(t + 1, src_next);
+            if (kt_next >= 0) issue(kt_next, src_next, lds0 + (cur ^ 1) * STAGEB);
+        }
+        if (kt >= 0 && qw0 < N && (!CAUSAL || kt <= qw0 + 31)) {
+            const unsigned char* buf = smem + cur * STAGEB;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const unsigned char* p0 = buf + (32 * kb + 16 * s2) * kLdsRowB;
+                    u32x4 y;
+                    {
+                        const u32x2 lo2 = lds_read_tr4(reinterpret_cast<const uint16_t*>(p0 + bt[0]));
+                        const u32x2 hi2 = lds_read_tr4(reinterpret_cast<const uint16_t*>(p0 + bt[1]));
+                        y[0] = lo2[0]; y[1] = lo2[1]; y[2] = hi2[0]; y[3] = hi2[1];
+                    }
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) {
+                        const u32x2 lo2 = lds_read_tr4(reinterpret_cast<const uint16_t*>(p0 + at[cb][0]));
+                        const u32x2 hi2 = lds_read_tr4(reinterpret_cast<const uint16_t*>(p0 + at[cb][1]));
+                        u32x4 x;
+                        x[0] = lo2[0]; x[1] = lo2[1]; x[2] = hi2[0]; x[3] = hi2[1];
+                        dq[cb] = mfma32(as_bf16x8(x), as_bf16x8(y), dq[cb]);
+                    }
+                }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of the next step
+        __syncthreads();
+        cur ^= 1;
+    }
+
+    const int qrow = qw0 + swap23(i);
+    if (qrow < N) {
+        uint16_t* dqr = p.dq + seq_off(sp, b, hh, p.dqsb, p.dqsh, p.dqsn) + (int64_t)qrow * p.dqsn;
+        const float sc = p.scale;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bf16x4 a;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] = (__bf16)(dq[cb][4 * j + e] * sc);
+                *reinterpret_cast<bf16x4*>(dqr + 32 * cb + 8 * j + 4 * hf) = a;
+            }
+    }
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
     const Layout& L = a.L;
@@ -1315,6 +1622,14 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const float c = a.scale * kLog2e;
+    const bool store_ds = D == 128 && a.ds != nullptr;
+    const int nqbt = (L.N + kQ_BQ - 1) / kQ_BQ;
+    if (store_ds && a.kv_offsets) {
+        hipLaunchKernelGGL(ds_pos_kernel, dim3((unsigned)((nqbt + 3) / 4)), dim3(256), 0, stream, a.kv_offsets,
+                           a.kv_indices, a.q_offsets, a.q_indices, a.nnz, nqbt, a.ds_pos);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     {
         KVParams p;
         p.q = static_cast<const uint16_t*>(a.q.p);
@@ -1342,6 +1657,9 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
         p.nkb = (L.N + kKV_BK - 1) / kKV_BK;
         p.c = c;
         p.scale = a.scale;
+        p.ds = store_ds ? a.ds : nullptr;
+        p.ds_bh = a.ds_bh;
+        p.nqbt = nqbt;
         const int64_t grid = (int64_t)L.B * L.Hkv * p.nkb;
         if constexpr (D == 128)
             hipLaunchKernelGGL((dkdv_pair_kernel<CAUSAL>), dim3((unsigned)grid), dim3(512), 0, stream, p);
@@ -1349,6 +1667,28 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
             hipLaunchKernelGGL((dkdv16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads16), 0, stream, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+    }
+    if (store_ds) {
+        DsQParams p;
+        p.k = static_cast<const uint16_t*>(a.k.p);
+        p.ds = a.ds;
+        p.pos = a.ds_pos;
+        p.dq = static_cast<uint16_t*>(a.dq);
+        p.ksb = a.k.sb; p.ksh = a.k.sh; p.ksn = a.k.sn;
+        p.dqsb = a.dqsb; p.dqsh = a.dqsh; p.dqsn = a.dqsn;
+        p.ds_bh = a.ds_bh;
+        p.B = L.B; p.H = L.H; p.N = L.N;
+        p.nqb = nqbt;
+        p.G = L.H / L.Hkv;
+        p.cu = L.cu;
+        p.total = L.total;
+        p.kv_offsets = a.kv_offsets;
+        p.kv_indices = a.kv_indices;
+        p.nnz = a.nnz;
+        p.scale = a.scale;
+        const int64_t grid = (int64_t)L.B * L.H * nqbt;
+        hipLaunchKernelGGL((dq_ds_kernel<CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+        return hipGetLastError();
     }
     {
         QParams p;

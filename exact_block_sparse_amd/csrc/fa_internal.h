@@ -66,6 +66,12 @@ struct BwdArgs {
     const int32_t* q_offsets;
     const int32_t* q_indices;
     int64_t nnz;
+    // Stored-dS mode (head dimension 128; nullptr: dQ recomputes S and dP): workspace regions
+    // for the dS tiles, ds_bh elements per (sequence, query head), and (block-sparse) one int32
+    // per list entry for the key-side position of each query-side entry.
+    uint16_t* ds = nullptr;
+    int64_t ds_bh = 0;
+    int32_t* ds_pos = nullptr;
 };
 
 // Launch the forward kernels on `stream`; returns hipSuccess or the launch error.

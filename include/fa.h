@@ -141,6 +141,14 @@ FA_API int fa_sparse_fwd(const void* q, const void* k, const void* v, void* o, f
 FA_API size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
 
 /*
+ * fa_bwd_ds_workspace_bytes - the workspace that lets fa_bwd keep dS instead of recomputing
+ * it (see fa_bwd): fa_bwd_workspace_bytes(...) plus B*H*T*32768 bytes, T = n(n+1)/2 causal or
+ * n*n otherwise with n = ceil(N / 128) (one bf16 128 x 128 tile per pair of key and query
+ * blocks the backward visits). 0 where that mode does not exist (d = 64, empty problems).
+ */
+FA_API size_t fa_bwd_ds_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int causal);
+
+/*
  * fa_bwd - attention backward by recomputation from the stored log-sum-exp.
  *
  * Defined in "Flash MSA Attention Kernel Implementation: A Practical Guide for Production
@@ -156,6 +164,14 @@ FA_API size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d)
  * workspace        : device buffer of at least fa_bwd_workspace_bytes(...) bytes,
  *                    16-byte aligned; its contents on entry are ignored.
  * Other arguments as in fa_fwd. The kernels are deterministic (no atomics).
+ *
+ * Two schedules compute this function. With workspace_bytes >= fa_bwd_ds_workspace_bytes(...)
+ * (> 0) the dK/dV pass, which forms every dS tile for the dK product anyway, also writes it
+ * (bf16, as rounded for that product) into the workspace, and the dQ pass reads it back: one
+ * matrix product per tile instead of three. With a smaller workspace the dQ pass recomputes
+ * S, P, dP and dS from Q, K, V, dO and the LSE. Both are exact up to rounding (the
+ * recomputed dS can differ from the stored one in the last bits of its fp32 value before
+ * bf16 rounding); each is deterministic.
  */
 FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv,
@@ -273,11 +289,25 @@ FA_API int fa_attn_fwd_visits(const fa_attn_desc* desc, const void* q, fa_stride
 FA_API size_t fa_attn_bwd_workspace_bytes(const fa_attn_desc* desc);
 
 /*
+ * fa_attn_bwd_ds_workspace_bytes - the workspace with which fa_attn_bwd keeps dS (the
+ * stored-dS schedule described at fa_bwd): fa_attn_bwd_workspace_bytes(desc), plus (block-
+ * sparse) nnz int32 rounded up to 256 bytes, plus B*H*T*32768 bytes of bf16 dS tiles with
+ * T = n(n+1)/2 dense causal, n*n dense non-causal (n = ceil(N / 128), N the longest
+ * sequence when packed) or nnz block-sparse. 0 where that schedule does not exist (head
+ * dimension 64, fp8, nnz = 0, empty problems, or more than 2^56 bytes).
+ */
+FA_API size_t fa_attn_bwd_ds_workspace_bytes(const fa_attn_desc* desc);
+
+/*
  * fa_attn_bwd - backward by recomputation (the function of fa_bwd) for any fa_attn_desc:
  * grouped heads (dk, dv have H_kv heads and sum over their query heads), packed sequences,
  * and block-sparse masks (kv_offsets / kv_indices for dQ, q_offsets / q_indices for dK and
  * dV; both describe the same pattern, which must be the one the forward used). o and lse
  * are the forward's outputs for the same desc. The kernels are deterministic (no atomics).
+ * A workspace of at least fa_attn_bwd_ds_workspace_bytes(desc) (> 0) selects the stored-dS
+ * schedule, as at fa_bwd; block-sparse, that schedule takes a query-side entry's dS from the
+ * key-side entry that names the same pair of blocks, so with lists that do not describe the
+ * same pattern, entries without such a mate contribute nothing to dQ.
  * Errors as in fa_bwd; FA_ERR_NULL also when block-sparse and q_offsets is NULL; FA_ERR_ARG
  * when dtype is not FA_DTYPE_BF16 (the backward is bf16).
  */
@@ -289,8 +319,8 @@ FA_API int fa_attn_bwd(const fa_attn_desc* desc, const void* q, fa_strides sq, c
 /*
  * fa_attn_bwd_noalloc - fa_attn_bwd for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid allocation. Same
- * arguments, function, kernels and results (bit for bit) as fa_attn_bwd, without the
- * workspace: the per-row values D_i it needs live in a device array the library owns, one
+ * arguments, function, kernels and results (bit for bit) as fa_attn_bwd with a workspace
+ * smaller than fa_attn_bwd_ds_workspace_bytes (dQ by recomputation), without the workspace: the per-row values D_i it needs live in a device array the library owns, one
  * per GPU, of FA_NOALLOC_WORKSPACE_BYTES, held until the process ends. The call allocates
  * nothing (no hipMalloc, hipFree or allocating library routine). Its first call on a device
  * looks up that device's array once (with the device current); later calls reuse it.

@@ -263,6 +263,33 @@ def test_attn_workspace_bytes(fa):
     assert fa.attn_bwd_workspace_bytes(2, 8, 1000, 128) == fa.bwd_workspace_bytes(2, 8, 1000, 128)
 
 
+def test_stored_ds_workspace_bytes(fa):
+    # the stored-dS schedule: base workspace + (sparse) nnz int32 rounded to 256 + one bf16
+    # 128 x 128 tile (32 KB) per (sequence, query head, visited pair of blocks)
+    base = fa.bwd_workspace_bytes(2, 32, 8192, 128)
+    assert fa.bwd_ds_workspace_bytes(2, 32, 8192, 128, causal=True) == base + 2 * 32 * (64 * 65 // 2) * 32768
+    assert fa.bwd_ds_workspace_bytes(2, 32, 8192, 128, causal=False) == base + 2 * 32 * 64 * 64 * 32768
+    n = -(-1000 // 128)
+    assert fa.bwd_ds_workspace_bytes(1, 3, 1000, 128, causal=True) == (
+        fa.bwd_workspace_bytes(1, 3, 1000, 128) + 3 * n * (n + 1) // 2 * 32768)
+    assert fa.bwd_ds_workspace_bytes(1, 3, 1000, 64, causal=True) == 0      # head dimension 64: recomputation only
+    assert fa.bwd_ds_workspace_bytes(0, 3, 1000, 128) == 0
+    lib = fa.lib
+    x = make_desc(fa, B=3, H=8, H_kv=2, N=700, cu_seqlens=16, total=1234, causal=1)
+    n = -(-700 // 128)
+    assert lib.fa_attn_bwd_ds_workspace_bytes(ctypes.byref(x)) == (
+        lib.fa_attn_bwd_workspace_bytes(ctypes.byref(x)) + 3 * 8 * n * (n + 1) // 2 * 32768)
+    nnz = 777
+    want = fa.attn_bwd_workspace_bytes(1, 16, 131072, 128) + (nnz * 4 + 255) // 256 * 256 + 16 * nnz * 32768
+    assert fa.attn_bwd_ds_workspace_bytes(1, 16, 131072, 128, causal=True, nnz=nnz) == want
+    assert fa.attn_bwd_ds_workspace_bytes(1, 16, 131072, 128, causal=True, nnz=0) == 0
+    assert lib.fa_attn_bwd_ds_workspace_bytes(None) == 0
+    x = make_desc(fa, B=1, H=1, H_kv=1, N=1 << 28, causal=0)                # 2^42 tiles of 32 KB: refused
+    assert lib.fa_attn_bwd_ds_workspace_bytes(ctypes.byref(x)) == 0
+    x.dtype = 1                                                              # fp8: no backward schedule stores dS
+    assert lib.fa_attn_bwd_ds_workspace_bytes(ctypes.byref(x)) == 0
+
+
 @pytest.mark.parametrize("nb,window,stride,causal,rule", [(1, 0, 0, True, "strided"), (37, 2, 5, True, "strided"),
                                                           (37, 2, 5, False, "fixed"), (64, 8, 16, True, "fixed"),
                                                           (20, 0, 0, False, "strided")])

@@ -94,15 +94,20 @@ GQA_BWD = [
 ]
 
 
+SCHEDULES = pytest.mark.parametrize("store_ds", [None, False], ids=["stored_ds", "recomputed"])
+
+
+@SCHEDULES
 @pytest.mark.parametrize("case", GQA_BWD, ids=lambda c: "b{}h{}kv{}n{}d{}{}".format(
     c[0], c[1], c[2], c[3], c[4], "c" if c[5] else ""))
-def test_gqa_backward_small(fa, case):
+def test_gqa_backward_small(fa, case, store_ds):
     B, H, Hkv, N, d, causal, sigma = case
     w = W.small(B, H, N, d, causal=causal, seed=13, H_kv=Hkv, direction="bwd", sigma=sigma)
     x = W.make_inputs(w)
     g = dev(x)
     o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], causal=causal, scale=w.scale)
-    dq, dk, dv = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], causal=causal, scale=w.scale)
+    dq, dk, dv = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], causal=causal, scale=w.scale,
+                             store_ds=store_ds)
     torch.cuda.synchronize()
     assert tuple(dk.shape) == tuple(x["k"].shape)
     dQ, dK, dV = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], causal=causal, scale=w.scale)
@@ -153,7 +158,8 @@ def test_varlen_single_sequence_equals_fixed_length(fa):
                                   ((129, 3, 256), 2, 1, 128, True)],
                          ids=lambda c: "{}_h{}kv{}d{}{}".format("-".join(map(str, c[0])), c[1], c[2], c[3],
                                                                 "c" if c[4] else ""))
-def test_varlen_backward_small(fa, case):
+@SCHEDULES
+def test_varlen_backward_small(fa, case, store_ds):
     # sigma 0.5: a one-row sequence makes dV the plain sum of its query heads' dO, which at
     # sigma 1 reaches the 4..8 range where bf16 output rounding alone uses 0.016 of the 0.02
     lens, H, Hkv, d, causal = case
@@ -163,7 +169,7 @@ def test_varlen_backward_small(fa, case):
     cu = w.cu_seqlens()
     o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], causal=causal, scale=w.scale, cu_seqlens=cu)
     dq, dk, dv = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], causal=causal, scale=w.scale,
-                             cu_seqlens=cu)
+                             cu_seqlens=cu, store_ds=store_ds)
     torch.cuda.synchronize()
     dQ, dK, dV = oracle.attention_backward_varlen(x["q"], x["k"], x["v"], x["do"], cu, causal=causal,
                                                   scale=w.scale)
@@ -201,7 +207,8 @@ SPARSE_BWD = [
 
 @pytest.mark.parametrize("case", SPARSE_BWD, ids=lambda c: "n{}h{}kv{}d{}{}w{}s{}{}".format(
     c[0], c[1], c[2], c[3], "c" if c[4] else "", c[5], c[6], c[7]))
-def test_sparse_backward_small(fa, case):
+@SCHEDULES
+def test_sparse_backward_small(fa, case, store_ds):
     N, H, Hkv, d, causal, window, stride, rule = case
     w = W.small(1, H, N, d, causal=causal, seed=18, H_kv=Hkv, direction="bwd")
     x = W.make_inputs(w)
@@ -210,7 +217,7 @@ def test_sparse_backward_small(fa, case):
     off, idx, sp = lists_for(nb, window, stride, causal, rule)
     o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], causal=causal, scale=w.scale, kv_offsets=off, kv_indices=idx)
     dq, dk, dv = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], causal=causal, scale=w.scale,
-                             kv_offsets=off, kv_indices=idx)
+                             kv_offsets=off, kv_indices=idx, store_ds=store_ds)
     torch.cuda.synchronize()
     dQ, dK, dV, O, L = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], causal=causal, scale=w.scale,
                                                  sparse=sp, return_forward=True)
@@ -259,8 +266,9 @@ def test_sparse_backward_hand_lists_with_empty_block(fa):
     assert_close("dV", dv, dV, TOL_OUT)
 
 
+@SCHEDULES
 @pytest.mark.parametrize("d", [64, 128])
-def test_sparse_backward_lists_with_entries_above_the_diagonal(fa, d):
+def test_sparse_backward_lists_with_entries_above_the_diagonal(fa, d, store_ds):
     # Device lists in which query blocks also name key blocks above them: under causal
     # masking those entries are skipped, so in the key-side lists a skipped query block comes
     # before the diagonal one. The dK/dV pass must still take the diagonal steps with the
@@ -277,7 +285,8 @@ def test_sparse_backward_lists_with_entries_above_the_diagonal(fa, d):
     to = lambda a: torch.from_numpy(a).to("cuda")
     kw = dict(causal=True, scale=w.scale, kv_offsets=to(off), kv_indices=to(idx))
     o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], **kw)
-    dq, dk, dv = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], q_offsets=to(t_off), q_indices=to(t_idx), **kw)
+    dq, dk, dv = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], q_offsets=to(t_off), q_indices=to(t_idx),
+                             store_ds=store_ds, **kw)
     torch.cuda.synchronize()
     sp = dict(block=128, offsets=off, indices=idx)
     dQ, dK, dV, O, L = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], causal=True, scale=w.scale,
@@ -304,7 +313,8 @@ def test_wrappers_refuse_mis_shaped_outputs(fa):
         fa.bwd(g["q"], g["k"], g["v"], o, lse.double(), g["do"], causal=True)
 
 
-def test_sparse_varlen_gqa_together(fa):
+@SCHEDULES
+def test_sparse_varlen_gqa_together(fa, store_ds):
     lens = (300, 700, 129)
     w = W.small(H=4, d=128, causal=True, seed=21, H_kv=2, seqlens=lens, direction="bwd", sigma=0.5)
     x = W.make_inputs(w)
@@ -314,7 +324,7 @@ def test_sparse_varlen_gqa_together(fa):
     off, idx, sp = lists_for(nb, 1, 3, True)
     kw = dict(causal=True, scale=w.scale, cu_seqlens=cu, kv_offsets=off, kv_indices=idx)
     o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], **kw)
-    dq, dk, dv = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], **kw)
+    dq, dk, dv = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], store_ds=store_ds, **kw)
     torch.cuda.synchronize()
     dQ, dK, dV, O, L = oracle.attention_backward_varlen(x["q"], x["k"], x["v"], x["do"], cu, causal=True,
                                                         scale=w.scale, sparse=sp, return_forward=True)

@@ -271,13 +271,19 @@ BWD_CASES = [
 ]
 
 
+# The two backward schedules: dS stored by the dK/dV pass and read back for dQ (the default
+# where it exists, head dimension 128), and dQ by recomputation (store_ds=False).
+SCHEDULES = pytest.mark.parametrize("store_ds", [None, False], ids=["stored_ds", "recomputed"])
+
+
+@SCHEDULES
 @pytest.mark.parametrize("B,H,N,d,causal,layout", BWD_CASES)
-def test_bwd_small(fa, B, H, N, d, causal, layout):
+def test_bwd_small(fa, B, H, N, d, causal, layout, store_ds):
     x = small_inputs(B, H, N, d, layout, seed=N + 1, grad=True)
     sc = scale_for(d)
     q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
     o, lse = fa.fwd(q, k, v, causal=causal, scale=sc)
-    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=sc)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=sc, store_ds=store_ds)
     torch.cuda.synchronize()
     dQ, dK, dV = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], causal=causal, scale=sc)
     assert_close("dQ", dq, dQ, TOL_OUT)
@@ -317,15 +323,41 @@ def test_packed_qkv_views(fa, causal, d):
         assert_close("sparse LSE", ls, Ls, TOL_LSE)
 
 
-def test_bwd_deterministic(fa):
+@SCHEDULES
+def test_bwd_deterministic(fa, store_ds):
     x = small_inputs(1, 2, 700, 128, seed=9, grad=True)
     q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
     o, lse = fa.fwd(q, k, v, causal=True)
-    a = fa.bwd(q, k, v, o, lse, do, causal=True)
-    b = fa.bwd(q, k, v, o, lse, do, causal=True)
+    a = fa.bwd(q, k, v, o, lse, do, causal=True, store_ds=store_ds)
+    b = fa.bwd(q, k, v, o, lse, do, causal=True, store_ds=store_ds)
     torch.cuda.synchronize()
     for x1, x2 in zip(a, b):
         assert torch.equal(x1, x2)
+
+
+def schedules_agree(fa, call):
+    """dK and dV come from the same pass in both schedules (bit for bit). dQ differs where a
+    recomputed dS rounds to another bf16 value than the stored one (the dK/dV pass forms dS
+    from an fp16 copy of P and accumulates dP onto -D; the dQ pass uses fp32 P and adds -D
+    after); over thousands of keys that stays within half the parity tolerance, or 2 units in
+    the last place of dQ's bf16 output where that is larger."""
+    a = call(store_ds=True)
+    b = call(store_ds=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    x, y = a[0].float(), b[0].float()
+    ulp = torch.exp2(torch.floor(torch.log2(y.abs().clamp_min(1e-30))) - 7)
+    excess = ((x - y).abs() - torch.clamp(2 * ulp, min=TOL_OUT / 2)).max().item()
+    assert excess <= 0, f"dQ of the two schedules differs by {excess} beyond 2 bf16 ulps"
+    return a
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_schedules_agree(fa, causal):
+    x = small_inputs(2, 3, 1000, 128, seed=31, grad=True)
+    q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=causal)
+    schedules_agree(fa, lambda **kw: fa.bwd(q, k, v, o, lse, do, causal=causal, **kw))
 
 
 # ----------------------------------------------------------------------------- benchmark workloads
@@ -409,8 +441,9 @@ def test_workload_bwd_b2h32_n8k(fa):
     x = W.make_inputs(w)
     q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
     o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
-    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale)
-    torch.cuda.synchronize()
+    # the stored-dS schedule (checked against the oracle below), and the recomputing one
+    # against it on every element
+    dq, dk, dv = schedules_agree(fa, lambda **kw: fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, **kw))
     for name, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
         assert_finite(name, t)
     # one head in full: every row of dQ, dK, dV against the oracle's own backward

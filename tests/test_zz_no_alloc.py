@@ -1,6 +1,7 @@
 """fa_attn_bwd_noalloc, the backward for callers that cannot allocate (its D workspace is a
 device array the library owns, one per GPU), against fa_attn_bwd with a caller-owned
-workspace: the same kernels on the same D values, so the outputs must be equal bit for bit.
+workspace too small for the stored-dS schedule: the same kernels on the same D values, so the
+outputs must be equal bit for bit.
 Two calls in a row, the second smaller, show that what the first left in the shared array
 does not matter; a third covers grouped heads, packed sequences and block lists together.
 """
@@ -35,7 +36,8 @@ def _compare(fa, w, **kw):
     g = {n: t.to("cuda") for n, t in x.items() if isinstance(t, torch.Tensor)}
     fwd_kw = {k: v for k, v in kw.items() if k not in ("q_offsets", "q_indices")}   # key-side lists: backward only
     o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], causal=w.causal, scale=w.scale, **fwd_kw)
-    want = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], causal=w.causal, scale=w.scale, **kw)
+    want = fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], causal=w.causal, scale=w.scale, store_ds=False,
+                       **kw)
     outs = [torch.full_like(t, float("nan")) for t in want]
     torch.cuda.synchronize()
     before = torch.cuda.memory_allocated()
