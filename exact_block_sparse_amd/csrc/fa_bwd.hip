@@ -19,13 +19,18 @@
 // 3. dq_dma_kernel (head dimension 128; dq_kernel at 64): a workgroup owns 128 query rows,
 //    as in the forward, and walks the key tiles: S^T = K Q^T and dP^T = V dO^T with Q and dO
 //    in registers, then dQ^T += K^T dS^T with K^T read transposed from the row-major K tile.
-// S and dP are thus computed twice (7 matrix products instead of 5) in exchange for no
-// atomics and bitwise-reproducible results.
+//    S and dP are thus computed twice (7 matrix products instead of 5) in exchange for no
+//    atomics and bitwise-reproducible results.
+// 3'. With a workspace large enough to hold every dS tile (head dimension 128), the dK/dV
+//    kernel (dkdv_pair_kernel, the head-dimension-128 replacement of dkdv16_kernel) also
+//    writes the bf16 dS it forms for the dK product, and dq_ds_kernel computes
+//    dQ^T += K^T dS^T from it: 5 products in all, still without atomics.
 //
 // LDS layouts, all free of bank conflicts for the reads they serve: the dK/dV kernel stages
 // its Q and dO tiles through registers into one copy with 288-byte rows, which serves both
 // its row reads and its transposing reads; dq_dma_kernel loads K and V straight into LDS as
-// unpadded rows with XOR-swizzled 16-byte chunks (one K copy for both read patterns);
+// unpadded rows with XOR-swizzled 16-byte chunks (one K copy for both read patterns), and
+// dq_ds_kernel K and the gathered dS rows the same way;
 // dq_kernel keeps a 272-byte row copy and a 320-byte transposed-read copy of K. Tiles are
 // fetched with raw buffer loads that zero-fill rows past N.
 #include <mutex>
