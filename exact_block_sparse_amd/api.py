@@ -81,13 +81,15 @@ def _bwd_workspace(ws, need: int, need_ds: int, store_ds, device) -> tuple[torch
     """Workspace of a backward call. A caller's tensor is used as given (its size selects the
     schedule in the library). Otherwise store_ds=True asks for the stored-dS schedule (an
     error where it does not exist), False for recomputation, and None takes the stored-dS
-    schedule when it exists and its workspace is at most a quarter of the device's memory."""
+    schedule when it exists and its workspace is at most a quarter of the device's memory
+    and half of what is free."""
     if ws is not None:
         return _workspace(ws, need, device)
     if store_ds and not need_ds:
         raise ValueError("the stored-dS backward needs head dimension 128, bf16 and a non-empty problem")
     if store_ds is None:
-        store_ds = 0 < need_ds <= torch.cuda.get_device_properties(device).total_memory // 4
+        free, total = torch.cuda.mem_get_info(device)
+        store_ds = 0 < need_ds <= min(total // 4, free // 2)
     return _workspace(None, need_ds if store_ds else need, device)
 
 
@@ -431,7 +433,7 @@ def attn_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None =
     the key-side lists are derived with ``transpose_block_lists`` when not given.
     ``store_ds`` picks the schedule when no workspace is given: True stores dS in the
     workspace (head dimension 128), False recomputes it in the dQ pass, None (default) stores
-    it when that workspace is at most a quarter of the device's memory.
+    it when that workspace is at most a quarter of the device's memory and half of what is free.
     """
     packed = cu_seqlens is not None
     _check_group(q, k, v, packed)
