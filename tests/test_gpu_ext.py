@@ -91,6 +91,7 @@ GQA_BWD = [
     # three query heads per K/V head, causal, N = 130: the last key block sees one query
     # step per head (an odd number of masked steps), the first an odd number of unmasked ones
     (1, 6, 2, 130, 128, True, 0.5),
+    (2, 6, 3, 300, 128, False, 1.0),
 ]
 
 
@@ -155,7 +156,7 @@ def test_varlen_single_sequence_equals_fixed_length(fa):
 
 
 @pytest.mark.parametrize("case", [((37, 0, 200, 1), 4, 2, 128, True), ((64, 100), 2, 2, 64, False),
-                                  ((129, 3, 256), 2, 1, 128, True)],
+                                  ((129, 3, 256), 2, 1, 128, True), ((300, 1, 129), 4, 2, 128, False)],
                          ids=lambda c: "{}_h{}kv{}d{}{}".format("-".join(map(str, c[0])), c[1], c[2], c[3],
                                                                 "c" if c[4] else ""))
 @SCHEDULES
@@ -202,6 +203,9 @@ SPARSE_BWD = [
     (640, 2, 2, 64, False, 1, 2, "fixed"),
     (900, 4, 2, 128, True, 2, 4, "strided"),
     (256, 1, 1, 128, True, 0, 0, "strided"),
+    # non-causal at head dimension 128 with grouped heads and a ragged end (the stored-dS
+    # schedule's key-tail zeros and above-diagonal tiles)
+    (700, 4, 2, 128, False, 1, 3, "strided"),
 ]
 
 
