@@ -580,3 +580,59 @@ def test_workload_fp8_h32_n32k(fa):
         O, L = oracle.attention_forward(sl("q"), sl("k"), sl("v"), causal=True, scale=w.scale, rows=rows)
         assert_close(f"O[h{h}]", o[0, h, rows], O[0, 0, rows], TOL_OUT)
         assert_close(f"LSE[h{h}]", lse[0, h, rows], L[0, 0, rows], TOL_LSE)
+
+
+# ----------------------------------------------------------------------------- seeded random mix
+def _random_case(rng):
+    d = int(rng.choice([64, 128]))
+    Hkv = int(rng.integers(1, 3))
+    H = Hkv * int(rng.integers(1, 4))
+    causal = bool(rng.integers(0, 2))
+    packed = bool(rng.integers(0, 2))
+    lens = tuple(int(x) for x in rng.integers(0, 600, size=int(rng.integers(1, 4)))) if packed else None
+    N = max(lens) if packed else int(rng.integers(1, 600))
+    if packed and N == 0:
+        lens, N = lens + (1,), max(1, N)
+    B = len(lens) if packed else int(rng.integers(1, 3))
+    sparse = bool(rng.integers(0, 2)) and N > 128
+    window, stride = int(rng.integers(0, 3)), int(rng.integers(0, 5))
+    return B, H, Hkv, N, d, causal, lens, sparse, window, stride
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_backward_seeded_random_mix(fa, seed):
+    """Forty seeded draws over head dimension, grouping, causality, packed lengths (empty and
+    one-row sequences included) and block lists; forward and both backward schedules against
+    the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    B, H, Hkv, N, d, causal, lens, sparse, window, stride = _random_case(rng)
+    sys.__stderr__.write(f"[case] B={B} H={H} Hkv={Hkv} N={N} d={d} causal={causal} lens={lens} "
+                         f"sparse={sparse} w={window} s={stride}\n")
+    w = W.small(B, H, N, d, causal=causal, seed=40 + seed, H_kv=Hkv, seqlens=lens, direction="bwd", sigma=0.5)
+    x = W.make_inputs(w)
+    g = dev(x)
+    kw = dict(causal=causal, scale=w.scale)
+    sp = None
+    if lens is not None:
+        kw["cu_seqlens"] = w.cu_seqlens()
+    if sparse:
+        nb = (N + 127) // 128
+        off, idx, sp = lists_for(nb, window, stride, causal)
+        kw.update(kv_offsets=off, kv_indices=idx)
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], **kw)
+    outs = {flag: fa.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], store_ds=flag, **kw)
+            for flag in ((None, False) if d == 128 else (False,))}
+    torch.cuda.synchronize()
+    if lens is not None:
+        dQ, dK, dV, O, L = oracle.attention_backward_varlen(x["q"], x["k"], x["v"], x["do"], w.cu_seqlens(),
+                                                            causal=causal, scale=w.scale, sparse=sp,
+                                                            return_forward=True)
+    else:
+        dQ, dK, dV, O, L = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], causal=causal,
+                                                     scale=w.scale, sparse=sp, return_forward=True)
+    assert_close("O", o, O, TOL_OUT)
+    assert_close("LSE", lse, L, TOL_LSE)
+    for dq, dk, dv in outs.values():
+        assert_close("dQ", dq, dQ, TOL_OUT)
+        assert_close("dK", dk, dK, TOL_OUT)
+        assert_close("dV", dv, dV, TOL_OUT)
