@@ -636,3 +636,35 @@ def test_backward_seeded_random_mix(fa, seed):
         assert_close("dQ", dq, dQ, TOL_OUT)
         assert_close("dK", dk, dK, TOL_OUT)
         assert_close("dV", dv, dV, TOL_OUT)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_forward_seeded_random_mix(fa, seed):
+    """Forty seeded draws for the forward (both layouts when not packed, scales other than
+    1/sqrt(d) included) against the oracle's output and LSE."""
+    rng = np.random.default_rng(2000 + seed)
+    B, H, Hkv, N, d, causal, lens, sparse, window, stride = _random_case(rng)
+    layout = "bhnd" if lens is not None or rng.integers(0, 2) else "bnhd"
+    sys.__stderr__.write(f"[case] B={B} H={H} Hkv={Hkv} N={N} d={d} causal={causal} lens={lens} "
+                         f"sparse={sparse} w={window} s={stride} layout={layout}\n")
+    w = W.small(B, H, N, d, causal=causal, seed=80 + seed, H_kv=Hkv, seqlens=lens, layout=layout)
+    x = W.make_inputs(w)
+    g = dev(x)
+    scale = float(w.scale * rng.choice([1.0, 0.5, 2.0]))
+    kw = dict(causal=causal, scale=scale)
+    sp = None
+    if lens is not None:
+        kw["cu_seqlens"] = w.cu_seqlens()
+    if sparse:
+        nb = (N + 127) // 128
+        off, idx, sp = lists_for(nb, window, stride, causal)
+        kw.update(kv_offsets=off, kv_indices=idx)
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], **kw)
+    torch.cuda.synchronize()
+    if lens is not None:
+        O, L = oracle.attention_forward_varlen(x["q"], x["k"], x["v"], w.cu_seqlens(), causal=causal, scale=scale,
+                                               sparse=sp)
+    else:
+        O, L = oracle.attention_forward(x["q"], x["k"], x["v"], causal=causal, scale=scale, sparse=sp)
+    assert_close("O", o, O, TOL_OUT)
+    assert_close("LSE", lse, L, TOL_LSE)
