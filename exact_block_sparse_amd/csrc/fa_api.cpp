@@ -300,6 +300,10 @@ int attn_bwd(const fa_attn_desc* desc, const void* q, fa_strides sq, const void*
     a.q_offsets = sparse ? d.q_offsets : nullptr;
     a.q_indices = sparse ? or_other(d.q_indices, d.q_offsets) : nullptr;
     a.nnz = sparse ? d.nnz : 0;
+    // A workspace that also holds the dS tiles selects the stored-dS schedule. Its layout
+    // after the per-row values (each part 256-byte aligned): block-sparse, the key-side
+    // position of every query-side entry; then the tiles, ds_bh elements per (sequence,
+    // query head).
     const size_t need_ds = allow_ds ? fa_attn_bwd_ds_workspace_bytes(desc) : 0;
     if (need_ds && workspace_bytes >= need_ds) {
         unsigned char* w = static_cast<unsigned char*>(workspace) + need;
