@@ -15,13 +15,14 @@ no CPU or eager fallback: a missing library raises at import, a bad argument rai
     o, lse, visits = attn_fwd_visits(q, k, v, kv_offsets=off, kv_indices=idx)   # + which listed tiles ran
     dq, dk, dv = attn_bwd(q, k, v, o, lse, do, kv_offsets=off, kv_indices=idx)   # sparse backward
     attn_bwd_noalloc(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv)   # library-owned workspace, no allocation
+    o = attention(q, k, v, causal=True); o.backward(do)   # autograd over attn_fwd / attn_bwd
 """
 from ._lib import EXPORTS, FA_STATUS, LIB_PATH, AttnDesc, FaError, Strides, lib
-from .api import (NOALLOC_WORKSPACE_BYTES, attn_bwd, attn_bwd_ds_workspace_bytes, attn_bwd_noalloc,
+from .api import (NOALLOC_WORKSPACE_BYTES, attention, attn_bwd, attn_bwd_ds_workspace_bytes, attn_bwd_noalloc,
                   attn_bwd_workspace_bytes, attn_fwd, attn_fwd_visits, bwd, bwd_ds_workspace_bytes, bwd_workspace_bytes,
                   check_block_lists, fwd, make_block_lists, sparse_fwd, status_str, transpose_block_lists)
 
-__all__ = ["fwd", "sparse_fwd", "bwd", "bwd_workspace_bytes", "bwd_ds_workspace_bytes", "attn_fwd", "attn_fwd_visits",
+__all__ = ["attention", "fwd", "sparse_fwd", "bwd", "bwd_workspace_bytes", "bwd_ds_workspace_bytes", "attn_fwd", "attn_fwd_visits",
            "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_ds_workspace_bytes", "attn_bwd_noalloc",
            "NOALLOC_WORKSPACE_BYTES",
            "make_block_lists", "check_block_lists", "transpose_block_lists", "status_str", "FaError", "Strides",

@@ -501,3 +501,36 @@ def attn_bwd_noalloc(q, k, v, o, lse, do, *, causal: bool = False, scale: float 
                                      _stream(q.device))
     check(st, "fa_attn_bwd_noalloc")
     return dq, dk, dv
+
+
+class _Attention(torch.autograd.Function):
+    """Autograd over attn_fwd / attn_bwd: the forward keeps O and the LSE (not the score
+    matrix), the backward hands them to the library's backward."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, kw, bwd_kw):
+        o, lse = attn_fwd(q, k, v, **kw)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.kw, ctx.bwd_kw = kw, bwd_kw
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        do = do if do.stride(-1) == 1 else do.contiguous()
+        dq, dk, dv = attn_bwd(q, k, v, o, lse, do, **ctx.kw, **ctx.bwd_kw)
+        return dq, dk, dv, None, None
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+              scale: float | None = None, cu_seqlens=None, max_seqlen: int | None = None, kv_offsets=None,
+              kv_indices=None, q_offsets=None, q_indices=None, block_size: int = BLOCK,
+              store_ds: bool | None = None) -> torch.Tensor:
+    """O = softmax(Q K^T scale + mask) V with gradients for q, k and v (bf16), for training: the
+    arguments of ``attn_fwd`` (dense, causal, grouped, packed, block-sparse); the backward runs
+    ``attn_bwd`` with ``store_ds`` and, block-sparse, the key-side lists (derived when not
+    given)."""
+    kw = dict(causal=causal, scale=scale, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, kv_offsets=kv_offsets,
+              kv_indices=kv_indices, block_size=block_size)
+    bwd_kw = dict(q_offsets=q_offsets, q_indices=q_indices, store_ds=store_ds)
+    return _Attention.apply(q, k, v, kw, bwd_kw)
