@@ -668,3 +668,35 @@ def test_forward_seeded_random_mix(fa, seed):
         O, L = oracle.attention_forward(x["q"], x["k"], x["v"], causal=causal, scale=scale, sparse=sp)
     assert_close("O", o, O, TOL_OUT)
     assert_close("LSE", lse, L, TOL_LSE)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_fp8_forward_seeded_random_mix(fa, seed):
+    """Twenty seeded draws of the fp8 forward (head dimension, grouping, causality, packed
+    lengths, block lists, layouts) against the oracle on the dequantized inputs."""
+    rng = np.random.default_rng(3000 + seed)
+    B, H, Hkv, N, d, causal, lens, sparse, window, stride = _random_case(rng)
+    layout = "bhnd" if lens is not None or rng.integers(0, 2) else "bnhd"
+    sys.__stderr__.write(f"[case] fp8 B={B} H={H} Hkv={Hkv} N={N} d={d} causal={causal} lens={lens} "
+                         f"sparse={sparse} w={window} s={stride} layout={layout}\n")
+    w = W.small(B, H, N, d, causal=causal, seed=120 + seed, H_kv=Hkv, seqlens=lens, layout=layout,
+                dtype="fp8_e4m3")
+    x = W.make_inputs(w)
+    g = {n: x[n].to("cuda") for n in "qkv"}
+    kw = dict(causal=causal, scale=w.scale)
+    sp = None
+    if lens is not None:
+        kw["cu_seqlens"] = w.cu_seqlens()
+    if sparse:
+        off, idx, sp = lists_for((N + 127) // 128, window, stride, causal)
+        kw.update(kv_offsets=off, kv_indices=idx)
+    o, lse = fa.attn_fwd(g["q"], g["k"], g["v"], **kw, **fp8_kw(x))
+    torch.cuda.synchronize()
+    if lens is not None:
+        O, L = oracle.attention_forward_varlen(dequant(x, "q"), dequant(x, "k"), dequant(x, "v"), w.cu_seqlens(),
+                                               causal=causal, scale=w.scale, sparse=sp)
+    else:
+        O, L = oracle.attention_forward(dequant(x, "q"), dequant(x, "k"), dequant(x, "v"), causal=causal,
+                                        scale=w.scale, sparse=sp)
+    assert_close("O", o, O, TOL_OUT)
+    assert_close("LSE", lse, L, TOL_LSE)
