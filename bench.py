@@ -357,8 +357,8 @@ def main():
         print(json.dumps({"copy_calibration_bytes": 2 * n, "launches": 5}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (heads and sequence "
-              "shards are independent per GPU; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (heads and sequence "
+              "shards would be independent per GPU). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
