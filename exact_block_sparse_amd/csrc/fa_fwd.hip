@@ -23,9 +23,11 @@
 //   swizzled per row; the other cases (head dimension 64, fp8) are staged through registers
 //   into padded rows (272-byte K rows, 320-byte V rows). Both layouts keep every LDS read
 //   free of bank conflicts on the 64-bank LDS;
-// * the running max is raised only when a tile's max exceeds it by more than 2^8 (in the
-//   exp2 domain): probabilities then stay below 256 and the O rescale becomes rare. The
-//   result is the same function; only the reference point of the exponentials moves;
+// * the running max is set by a row's first tile and raised only when a tile's
+//   probabilities would pass 2^64 (in the exp2 domain), detected from the tile's row-sum
+//   parts rather than from a tile max; the O rescale becomes rare and no step computes a
+//   max over its scores. The result is the same function; only the reference point of the
+//   exponentials moves;
 // * O^T = V^T P^T accumulates in fp32 registers; P is rounded to bf16 only as an MFMA
 //   operand; exp is computed as exp2 with scale*log2(e) folded into one FMA;
 // * dense kernel ("ping-pong"): 8 waves and 256 query rows per workgroup, in two groups of
@@ -46,7 +48,7 @@ namespace {
 
 constexpr int kBK = 64;            // keys per pipeline step
 constexpr int kSparseBlock = 128;
-constexpr float kRescaleSlack = 8.0f;   // log2 of the largest probability allowed before a rescale
+constexpr float kSumLimit = 0x1p64f;    // largest part of a tile's row sum allowed without a rescale
 
 template <int D, bool F8 = false>
 struct Cfg {
@@ -198,7 +200,8 @@ struct Rows {
     float m_run;            // running max (exp2 domain)
     float l4[4];            // this lane's row sum in four interleaved parts (short add chains)
     float m_neg;            // -m_run, or 0 while m_run is -inf (the exponent's offset)
-    float m_thr;            // m_run + the rescale slack: a tile max above it raises m_run
+    float t_thr;            // a part of a tile's row sum above it raises m_run: -1 while
+                            // m_run is -inf (every tile then sets it), else kSumLimit
     f32x16 s[2];            // scores of the current 64-key step (two 32-key blocks)
     bf16x8 pb[2][2];        // probabilities of the current step as bf16 B operands
 };
@@ -255,8 +258,34 @@ __device__ __forceinline__ void scores(const uint16_t* buf, Rows<D, F8>& w, int 
     }
 }
 
-// Online softmax update for one step: mask (diagonal or tail tiles only), tile max, lazy
-// rescale, probabilities, fp32 row sum, bf16 operands. `masked` is uniform across the wave.
+// Probabilities of one step against the current running max, their sums in the lane's four
+// row-sum parts (t4, this tile only) and their bf16 MFMA operands.
+template <int D, bool F8>
+__device__ __forceinline__ void probs(Rows<D, F8>& w, float ce, float (&t4)[4]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            float pr[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pr[e] = fast_exp2(fmaf(w.s[kb][8 * st + e], ce, w.m_neg));
+                t4[e & 3] = (kb == 0 && st == 0 && e < 4) ? pr[e] : t4[e & 3] + pr[e];
+            }
+            w.pb[kb][st] = pack8(pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]);
+        }
+}
+
+// Online softmax update for one step: mask (diagonal or tail tiles only), probabilities,
+// fp32 row sum, bf16 operands, and the running max. `masked` is uniform across the wave.
+//
+// The running max is only a reference point for the exponent: any value at or below the
+// true row max gives the same normalised result, as long as no probability overflows. So
+// it is set from the first tile that has a key and afterwards raised only when a tile's
+// probabilities grow past 2^64 (far inside fp32 and bf16 range even summed over 2^20 keys).
+// That is detected from the tile's row-sum parts, which bound each of their terms, instead
+// of a tile max over all 32 scores every step; on the rare tile that trips it the scores
+// are still in registers and the step is redone against its own max.
 template <int D, bool F8, bool CAUSAL>
 __device__ __forceinline__ void softmax(Rows<D, F8>& w, bool masked, int kt0, int qrow, int N, float c,
                                         int hf) {
@@ -280,50 +309,39 @@ __device__ __forceinline__ void softmax(Rows<D, F8>& w, bool masked, int kt0, in
             }
         ce = 1.0f;
     }
-    // Tile max of the scaled scores: the scale is never negative here (the kernels flip
-    // the sign of Q instead), so it is the scaled max of the raw scores. The NaN-propagating
-    // maximum needs no quieting of its inputs.
-    float mt = __builtin_elementwise_maximum(w.s[0][0], w.s[1][0]);
+    // The row sum is taken in fp32 over the unrounded probabilities (the LSE needs it);
+    // P is rounded to bf16 only as the MFMA operand.
+    float t4[4];
+    probs(w, ce, t4);
+    const float tmax = __builtin_elementwise_maximum(__builtin_elementwise_maximum(t4[0], t4[1]),
+                                                     __builtin_elementwise_maximum(t4[2], t4[3]));
+    if (__any(tmax > w.t_thr)) {
+        // Tile max of the scaled scores: the scale is never negative here (the kernels flip
+        // the sign of Q instead), so it is the scaled max of the raw scores. The
+        // NaN-propagating maximum needs no quieting of its inputs (a NaN row keeps its max).
+        float mt = __builtin_elementwise_maximum(w.s[0][0], w.s[1][0]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mt = __builtin_elementwise_maximum(mt, w.s[kb][r]);
-    mt = pair_max(mt);
-    mt *= ce;
-
-    // Raise the running max only when the tile would push a probability above 2^8.
-    const bool need = mt > w.m_thr;
-    if (__any(need)) {
+            for (int r = 1; r < 16; ++r) mt = __builtin_elementwise_maximum(mt, w.s[kb][r]);
+        mt = pair_max(mt);
+        mt *= ce;
+        const bool need = mt > w.m_run;
         const float m_new = need ? mt : w.m_run;
         const float alpha = need ? fast_exp2(w.m_run - m_new) : 1.0f;
         w.m_run = m_new;
         w.m_neg = (m_new == kNegInf) ? 0.0f : -m_new;
-        w.m_thr = m_new + kRescaleSlack;
+        w.t_thr = (m_new == kNegInf) ? -1.0f : kSumLimit;
 #pragma unroll
         for (int j = 0; j < 4; ++j) w.l4[j] *= alpha;
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) w.o[cb][r] *= alpha;
+        probs(w, ce, t4);
     }
-
-    // The row sum is taken in fp32 over the unrounded probabilities (the LSE needs it);
-    // P is rounded to bf16 only as the MFMA operand.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float pr = fast_exp2(fmaf(w.s[kb][r], ce, w.m_neg));
-            w.s[kb][r] = pr;
-            w.l4[r & 3] += pr;
-        }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-            w.pb[kb][st] = pack8(w.s[kb][8 * st + 0], w.s[kb][8 * st + 1], w.s[kb][8 * st + 2],
-                                 w.s[kb][8 * st + 3], w.s[kb][8 * st + 4], w.s[kb][8 * st + 5],
-                                 w.s[kb][8 * st + 6], w.s[kb][8 * st + 7]);
+    for (int j = 0; j < 4; ++j) w.l4[j] += t4[j];
 }
 
 // O^T += V^T P^T. B element e of k-step st in half hf is key 16*st + 8*(e/4) + 4*hf + e%4 of
@@ -387,7 +405,7 @@ __device__ __forceinline__ void load_q(Rows<D, F8>& w, const typename ElemOf<F8>
     for (int cb = 0; cb < C::CB; ++cb) w.o[cb] = f32x16{};
     w.m_run = kNegInf;
     w.m_neg = 0.0f;
-    w.m_thr = kNegInf;
+    w.t_thr = -1.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) w.l4[j] = 0.0f;
 }

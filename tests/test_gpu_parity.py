@@ -260,6 +260,26 @@ def test_fwd_scores_far_above_the_first_tile(fa, causal):
     assert_close("LSE", lse, L, TOL_LSE)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_scores_well_above_the_first_tile(fa, causal):
+    # Keys after the first 64 scaled up 8x: later scores exceed the first tile's maximum by
+    # 20-50 in the exp2 domain, below the point where the running max must move, so those
+    # tiles' probabilities reach 2^20-2^49 in the products and the row sum unrescaled.
+    x = small_inputs(1, 2, 300, 128, seed=41)
+    k = x["k"].float()
+    k[:, :, 64:] *= 8.0
+    k = k.to(torch.bfloat16)
+    sc = scale_for(128)
+    o, lse = fa.fwd(to_dev(x["q"]), to_dev(k), to_dev(x["v"]), causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_forward(x["q"], k, x["v"], causal=causal, scale=sc)
+    S = sc * np.log2(np.e) * np.einsum("bhid,bhjd->bhij", f64(x["q"]), f64(k))
+    gap = S[..., 64:, 64:].max(axis=-1) - S[..., 64:, :64].max(axis=-1)
+    assert 40 < gap.max() < 56
+    assert_close("O", o, O, TOL_OUT)
+    assert_close("LSE", lse, L, TOL_LSE)
+
+
 # ----------------------------------------------------------------------------- backward, small
 BWD_CASES = [
     (1, 1, 64, 64, False, "bhnd"),
