@@ -903,8 +903,15 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(KVParams p) {
     if (pwave) {
         auto iterate = [&](auto masked_c) {
             const bool active = t < n_all;
-            f32x16 sacc[2] = {f32x16{}, f32x16{}};
-            if (active) row_products(stage_of(t), sacc);
+            // S starts at zero inside the branch: initialised outside it, the zeros (which the
+            // first product takes as an inline constant anyway) were written to 32 registers
+            // every iteration for the inactive path's sake
+            f32x16 sacc[2];
+            if (active) {
+                sacc[0] = f32x16{};
+                sacc[1] = f32x16{};
+                row_products(stage_of(t), sacc);
+            }
             __syncthreads();   // the dS waves have read the exchange buffer
             bf16x8 pb[2][2];
             if (active) {
