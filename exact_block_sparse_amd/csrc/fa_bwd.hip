@@ -543,6 +543,11 @@ constexpr int kPairStatB = 2 * kStep * 4;                      // lse2[64], -D[6
 constexpr int kPairStageB = 2 * kLdsTileB + kPairStatB;       // Q | dO | lse2 | -D
 constexpr int kPairXB = 4 * kStep * 32 * 2;                   // P of one step for four key groups, fp16
 
+// Pointers into global memory that stay global (not generic) after passing through an
+// empty asm statement, so that stores through them remain global stores.
+using GlobalU16 = __attribute__((address_space(1))) uint16_t;
+using GlobalU32x4 = __attribute__((address_space(1))) u32x4;
+
 template <bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(KVParams p) {
     constexpr int D = 128;
@@ -843,7 +848,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(KVParams p) {
     bool sv_masked = m_per > 0;
     const bool tail_block = k0 + kKV_BK > N;   // uniform: some of the block's keys are past the end
     const bool key_out = key >= N;
-    auto store_ds = [&](bf16x8 (&db)[2][2]) {
+    // The address of the step's dS tile half for this lane; advances the store iterator.
+    // Computed early in the iteration, where the dS waves would otherwise wait for the P
+    // waves' S products, so that only the stores remain behind the gradient products.
+    auto ds_address = [&]() -> uint16_t* {
         int64_t tile;
         int half;
         if (!steps.sparse) {
@@ -861,6 +869,16 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(KVParams p) {
         }
         uint16_t* dst = p.ds + ((int64_t)b * p.H + (h0 + sv_gq)) * p.ds_bh + tile * (kKV_BK * 128) +
                         half * 8192 + grp * 2048 + lane * 8;
+        if (++sv_j == (sv_masked ? m_per : u_per)) {
+            sv_j = 0;
+            if (++sv_gq == G) {
+                sv_gq = 0;
+                sv_masked = false;
+            }
+        }
+        return dst;
+    };
+    auto store_ds = [&](bf16x8 (&db)[2][2], GlobalU16* dst) {
         if (tail_block) {
             asm volatile("");   // a branch, not selects on every step: only the last key block has such keys
             if (key_out) {
@@ -876,14 +894,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(KVParams p) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
                 __builtin_nontemporal_store(__builtin_bit_cast(u32x4, db[m][s2]),
-                                            reinterpret_cast<u32x4*>(dst + 512 * (2 * m + s2)));
-        if (++sv_j == (sv_masked ? m_per : u_per)) {
-            sv_j = 0;
-            if (++sv_gq == G) {
-                sv_gq = 0;
-                sv_masked = false;
-            }
-        }
+                                            reinterpret_cast<GlobalU32x4*>(dst + 512 * (2 * m + s2)));
     };
 
     if (!pwave) {
@@ -929,6 +940,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(KVParams p) {
         while (t <= n_all) {
             bf16x8 db[2][2];
             if (t >= 1) ds_values(db);
+            GlobalU16* ds_dst = nullptr;
+            if (t >= 1 && p.ds != nullptr) {
+                ds_dst = (GlobalU16*)ds_address();
+                asm volatile("" : "+v"(ds_dst));   // keep the address work here, not at the stores
+            }
             // stores before the loads: the waits below then leave only step t + 2's loads in
             // flight and cover these stores too
             const bool more = t + 2 < n_all;
@@ -943,7 +959,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(KVParams p) {
             } else {
                 __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
             }
-            if (t >= 1 && p.ds != nullptr) store_ds(db);
+            if (t >= 1 && p.ds != nullptr) store_ds(db, ds_dst);
             __syncthreads();
             ++t;
         }
