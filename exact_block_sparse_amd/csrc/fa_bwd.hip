@@ -513,9 +513,8 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
 //   dV^T += dO^T P, and hands P to its partner through LDS as fp16 (P <= 1; rounding to
 //   nearest loses at most 2^-11 of it, a quarter of what bf16 would, so dS = P (dP - D)
 //   keeps nearly the accuracy of an fp32 P, which would not fit the LDS budget);
-// * the dS wave (waves 4-7), one step behind, computes dS = P o (dP - D) and dK^T += Q^T dS,
-//   and then dP - D of the step the P wave is on (its accumulators start at -D), kept in
-//   registers for the next iteration.
+// * the dS wave (waves 4-7) computes dP - D of a step (its accumulators start at -D), kept in
+//   registers until P arrives, then dS = P o (dP - D) and dK^T += Q^T dS.
 // Every product is a 32x32x16 one with the lane's key as its column: K (P wave) or V (dS
 // wave) rows of the key are register B operands of S and dP, whose accumulators (rows =
 // queries) turn into the B operands of the gradient products without any exchange between
@@ -524,19 +523,21 @@ __global__ __launch_bounds__(kThreads16, 1) void dkdv16_kernel(KVParams p) {
 // read patterns are free of bank conflicts. Against 16 keys per wave on 16x16x32 products,
 // this reads a quarter of the LDS bytes per product.
 //
-// An iteration t has two barriers. Before the first, the P waves run S(t) on the matrix
-// cores while the dS waves read P(t - 1) and form dS; after it, the P waves form P(t) (and
-// overwrite the single exchange buffer) and issue the loads of step t + 2 while the dS waves
-// run dK(t - 1) and dP(t); then the P waves run dV(t). So the vector work of each kind of
-// wave sits beside the other's matrix products. Tiles travel from memory straight into LDS
-// (four stages: the P waves read step t, the dS waves step t - 1, steps t + 1 and t + 2 are
-// loading), with the step's LSE (pre-converted to the exp2 domain by pre_kernel) and -D rows.
-// Only the dS waves load, right before the first barrier, where they would otherwise wait
-// for the P waves' S products: issuing the loads of a step stalls a wave for hundreds of
-// cycles while the address path works through them, and there it costs nothing. Product
-// phases run at raised wave priority, so that they issue ahead of the neighbour's vector
-// work. Rows past the sequence end read as zeros, which makes their contributions exactly 0
-// (zero dO rows for dV; dP = 0 and D = 0 for dK).
+// The two kinds of wave alternate as in the forward: an iteration t has two phases, each
+// with one kind of wave on the matrix cores and the other on its vector work. Phase A: the
+// P waves run dV(t) (P(t) kept in registers from the previous phase) and S(t + 1), while the
+// dS waves read P(t) from the single exchange buffer, form dS(t) and issue the loads of step
+// t + 3. Phase B, after a barrier: the P waves form P(t + 1) and overwrite the exchange
+// buffer, while the dS waves run dK(t) and dP(t + 1) (kept in registers for the next phase
+// A). So every phase holds 32 products per SIMD, and the vector work of each kind of wave
+// sits beside the other's products. Tiles travel from memory straight into LDS (four
+// stages: steps t and t + 1 are read, t + 2 and t + 3 are loading), with the step's LSE
+// (pre-converted to the exp2 domain by pre_kernel) and -D rows. Only the dS waves load, in
+// phase A, where their own work is vector work: issuing the loads of a step stalls a wave
+// for hundreds of cycles while the address path works through them. Product phases run at
+// raised wave priority, so that they issue ahead of the neighbour's vector work. Rows past
+// the sequence end read as zeros, which makes their contributions exactly 0 (zero dO rows
+// for dV; dP = 0 and D = 0 for dK).
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 constexpr int kPairStages = 4;
 constexpr int kPairStatB = 2 * kStep * 4;                      // lse2[64], -D[64]
@@ -904,62 +905,58 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(KVParams p) {
     // Settle every outstanding load (the K/V rows and steps 0 and 1) before the loop.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // Iteration t (two barriers, see above). Stage of step s: s % 4; the loads of step t + 2
-    // go to the stage of step t - 2, last read by the dS waves in iteration t - 1. Each kind of
-    // wave runs its own copy of the loop (the same iterations and barriers), so that neither
-    // holds the other's registers. The P waves take the masked steps first, in a loop of their
-    // own, so that the others carry no element test.
-    int t = 0;
+    // Iterations t = -1 .. n_all - 1 (two phases each, see above; iteration -1 only starts
+    // step 0). Stage of step s: s % 4; the loads of step t + 3 go to the stage of step t - 1,
+    // last read in iteration t - 1. Each kind of wave runs its own copy of the loop (the same
+    // iterations and barriers), so that neither holds the other's registers. The P waves take
+    // the masked steps first, in a loop of their own, so that the others carry no element test.
+    int t = -1;
     auto stage_of = [&](int s) -> uint32_t { return (uint32_t)((s & (kPairStages - 1)) * kPairStageB); };
     if (pwave) {
+        bf16x8 pb[2][2];   // P(t) as bf16 B operands, from phase B of iteration t - 1 to dV(t)
         auto iterate = [&](auto masked_c) {
-            const bool active = t < n_all;
-            // S starts at zero inside the branch: initialised outside it, the zeros (which the
-            // first product takes as an inline constant anyway) were written to 32 registers
-            // every iteration for the inactive path's sake
+            const int tn = t + 1;
+            if (t >= 0) grad_products(stage_of(t), pb);   // dV(t)
             f32x16 sacc[2];
-            if (active) {
+            if (tn < n_all) {
                 sacc[0] = f32x16{};
                 sacc[1] = f32x16{};
-                row_products(stage_of(t), sacc);
+                row_products(stage_of(tn), sacc);          // S(t + 1)
             }
             __syncthreads();   // the dS waves have read the exchange buffer
-            bf16x8 pb[2][2];
-            if (active) {
+            if (tn < n_all) {
                 // masked steps (the first n_mask): the diagonal block's halves, m_per per head
-                const int r0 = k0 + (m_per == 2 ? (t & 1) : 0) * kStep;
-                probs(masked_c, stage_of(t), r0, sacc, pb);
-                grad_products(stage_of(t), pb);
+                const int r0 = k0 + (m_per == 2 ? (tn & 1) : 0) * kStep;
+                probs(masked_c, stage_of(tn), r0, sacc, pb);
             }
             __syncthreads();
             ++t;
         };
-        while (t < n_mask) iterate(std::true_type{});
-        while (t <= n_all) iterate(std::false_type{});
+        while (t + 1 < n_mask) iterate(std::true_type{});
+        while (t < n_all) iterate(std::false_type{});
     } else {
-        while (t <= n_all) {
+        while (t < n_all) {
+            const int tn = t + 1;
             bf16x8 db[2][2];
-            if (t >= 1) ds_values(db);
+            if (t >= 0) ds_values(db);
             GlobalU16* ds_dst = nullptr;
-            if (t >= 1 && p.ds != nullptr) {
+            if (t >= 0 && p.ds != nullptr) {
                 ds_dst = (GlobalU16*)ds_address();
                 asm volatile("" : "+v"(ds_dst));   // keep the address work here, not at the stores
             }
-            // stores before the loads: the waits below then leave only step t + 2's loads in
-            // flight and cover these stores too
-            const bool more = t + 2 < n_all;
-            if (more) issue_next(lds0 + stage_of(t + 2));
+            const bool more = t + 3 < n_all;
+            if (more) issue_next(lds0 + stage_of(t + 3));
             __syncthreads();   // the exchange buffer is read; the P waves may overwrite it
-            if (t >= 1) grad_products(stage_of(t - 1), db);
-            if (t < n_all) dp_products(stage_of(t));
-            // step t + 1 must have arrived; step t + 2's loads may stay in flight
+            if (t >= 0) grad_products(stage_of(t), db);   // dK(t)
+            if (tn < n_all) dp_products(stage_of(tn));    // dP(t + 1)
+            // step t + 2 must have arrived; step t + 3's loads may stay in flight
             if (more) {
                 if (stat_wave) __builtin_amdgcn_s_waitcnt(0x0F70 | 9);   // vmcnt(9)
                 else __builtin_amdgcn_s_waitcnt(0x0F70 | 8);             // vmcnt(8)
             } else {
                 __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
             }
-            if (t >= 1 && p.ds != nullptr) store_ds(db, ds_dst);
+            if (t >= 0 && p.ds != nullptr) store_ds(db, ds_dst);
             __syncthreads();
             ++t;
         }
