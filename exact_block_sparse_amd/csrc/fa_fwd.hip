@@ -24,9 +24,9 @@
 //   into padded rows (272-byte K rows, 320-byte V rows). Both layouts keep every LDS read
 //   free of bank conflicts on the 64-bank LDS;
 // * the running max is set by a row's first tile and raised only when a tile's
-//   probabilities would pass 2^64 (in the exp2 domain), detected from the tile's row-sum
-//   parts rather than from a tile max; the O rescale becomes rare and no step computes a
-//   max over its scores. The result is the same function; only the reference point of the
+//   probabilities pass 2^8 (in the exp2 domain), detected from the tile's row-sum parts
+//   rather than from a tile max; the O rescale stays rare and no step computes a max over
+//   its scores. The result is the same function; only the reference point of the
 //   exponentials moves;
 // * O^T = V^T P^T accumulates in fp32 registers; P is rounded to bf16 only as an MFMA
 //   operand; exp is computed as exp2 with scale*log2(e) folded into one FMA;
@@ -48,7 +48,7 @@ namespace {
 
 constexpr int kBK = 64;            // keys per pipeline step
 constexpr int kSparseBlock = 128;
-constexpr float kSumLimit = 0x1p64f;    // largest part of a tile's row sum allowed without a rescale
+constexpr float kSumLimit = 0x1p8f;     // largest part of a tile's row sum allowed without a rescale
 
 template <int D, bool F8 = false>
 struct Cfg {
@@ -281,11 +281,14 @@ __device__ __forceinline__ void probs(Rows<D, F8>& w, float ce, float (&t4)[4]) 
 //
 // The running max is only a reference point for the exponent: any value at or below the
 // true row max gives the same normalised result, as long as no probability overflows. So
-// it is set from the first tile that has a key and afterwards raised only when a tile's
-// probabilities grow past 2^64 (far inside fp32 and bf16 range even summed over 2^20 keys).
-// That is detected from the tile's row-sum parts, which bound each of their terms, instead
-// of a tile max over all 32 scores every step; on the rare tile that trips it the scores
-// are still in registers and the step is redone against its own max.
+// it is set from the first tile that has a key and afterwards raised only when a part of a
+// tile's row sum passes 2^8. That is detected from the tile's row-sum parts, which bound
+// each of their terms, instead of a tile max over all 32 scores every step; on the rare
+// tile that trips it the scores are still in registers and the step is redone against its
+// own max. Range alone would allow far more (2^64 keeps fp32 and bf16 safe), but a row
+// dominated by a few keys is only as accurate as their bf16-rounded probabilities, which
+// are exact (1) for the key that set the max: letting the max lag far behind made such
+// rows' outputs less accurate, so the limit keeps the old bound on each probability.
 template <int D, bool F8, bool CAUSAL>
 __device__ __forceinline__ void softmax(Rows<D, F8>& w, bool masked, int kt0, int qrow, int N, float c,
                                         int hf) {
