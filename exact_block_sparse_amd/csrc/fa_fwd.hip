@@ -413,16 +413,27 @@ __device__ __forceinline__ void load_q(Rows<D, F8>& w, const typename ElemOf<F8>
     for (int j = 0; j < 4; ++j) w.l4[j] = 0.0f;
 }
 
+// Row pitch of the epilogue's LDS staging area (bytes; the 16-byte pad keeps the row writes
+// of the 32 lanes of a half on distinct banks) and the area of one wave (its 32 rows).
+template <int D> constexpr uint32_t kEpiPitch = 2 * D + 16;
+template <int D> constexpr uint32_t kEpiWaveB = 32 * kEpiPitch<D>;
+
 // O = O^T / l as bf16; LSE = (m + log2 l) * ln 2. `obase` and `lbase` point at row 0 of the
-// sequence's head.
+// sequence's head. A lane holds 4-value pieces of one row, so stored directly every store
+// instruction would write 64 scattered 8-byte pieces; instead the wave writes its 32 rows
+// into its own LDS area (`lds_wave`: all LDS reads of the loop are done, which the loop's
+// last barrier guarantees) and stores whole rows from there, 16 lanes per row, 16 bytes
+// each. The wave only reads back what it wrote, so no barrier is needed (a wave's LDS
+// operations complete in order; the wait below is only for the compiler's benefit).
 template <int D, bool F8>
 __device__ __forceinline__ void epilogue(const Rows<D, F8>& w, uint16_t* obase, int64_t osn, float* lbase, int qrow,
-                                         int N, int hf, float vdesc) {
+                                         int N, int hf, float vdesc, uint32_t lds_wave, int i) {
     using C = Cfg<D, F8>;
+    constexpr uint32_t PITCH = kEpiPitch<D>;
+    constexpr int CHUNKS = D / 8;              // 16-byte pieces of a row
+    constexpr int ROWS = 64 / CHUNKS;          // rows per store instruction
     const float l_tot = pair_sum((w.l4[0] + w.l4[1]) + (w.l4[2] + w.l4[3]));
-    if (qrow >= N) return;
     const float inv = l_tot > 0.0f ? vdesc / l_tot : 0.0f;
-    uint16_t* orow = obase + (int64_t)qrow * osn;
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
@@ -432,9 +443,18 @@ __device__ __forceinline__ void epilogue(const Rows<D, F8>& w, uint16_t* obase, 
             val[1] = (__bf16)(w.o[cb][4 * j + 1] * inv);
             val[2] = (__bf16)(w.o[cb][4 * j + 2] * inv);
             val[3] = (__bf16)(w.o[cb][4 * j + 3] * inv);
-            *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * j + 4 * hf) = val;
+            *(__attribute__((address_space(3))) bf16x4*)(uintptr_t)(lds_wave + i * PITCH +
+                                                                    2 * (32 * cb + 8 * j + 4 * hf)) = val;
         }
-    if (hf == 0) lbase[qrow] = l_tot > 0.0f ? (w.m_run + log2f(l_tot)) * kLn2 : kNegInf;
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    const int lane = 32 * hf + i, qw0 = qrow - i, ch = lane % CHUNKS;
+#pragma unroll
+    for (int k = 0; k < 32 / ROWS; ++k) {
+        const int r = k * ROWS + lane / CHUNKS;
+        const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(lds_wave + r * PITCH + 16 * ch);
+        if (qw0 + r < N) *reinterpret_cast<u32x4*>(obase + (int64_t)(qw0 + r) * osn + 8 * ch) = v;
+    }
+    if (hf == 0 && qrow < N) lbase[qrow] = l_tot > 0.0f ? (w.m_run + log2f(l_tot)) * kLn2 : kNegInf;
 }
 
 // ----------------------------------------------------------------------------- dense, ping-pong
@@ -468,6 +488,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_kernel(Params p) {
     using C = Cfg<D, F8>;
     using E = typename ElemOf<F8>::type;
     __shared__ __attribute__((aligned(16))) uint16_t smem[kPPBufs * C::BUF];
+    static_assert(sizeof(smem) >= (kPPThreads / 64) * kEpiWaveB<D>, "the epilogue stages every wave's rows in LDS");
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, i = lane & 31;
@@ -541,7 +562,8 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_kernel(Params p) {
         __syncthreads();
     }
     epilogue<D, F8>(w, p.o + seq_off(sp, b, hh, p.osb, p.osh, p.osn), p.osn,
-                    p.lse + seq_stat_off(sp, b, hh, p.H, p.N, p.total), qrow, N, hf, p.vdesc);
+                    p.lse + seq_stat_off(sp, b, hh, p.H, p.N, p.total), qrow, N, hf, p.vdesc,
+                    lds_address(smem) + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * kEpiWaveB<D>, i);
 }
 
 // ----------------------------------------------------------------------------- dense, ping-pong,
@@ -649,6 +671,7 @@ template <bool CAUSAL>
 __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_dma_kernel(Params p) {
     constexpr int D = 128;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[kDmaBufs * kDmaStageB];
+    static_assert(sizeof(smem) >= (kPPThreads / 64) * kEpiWaveB<D>, "the epilogue stages every wave's rows in LDS");
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, i = lane & 31;
@@ -725,7 +748,8 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_dma_kernel(Params 
         __syncthreads();
     }
     epilogue<D, false>(w, p.o + seq_off(sp, b, hh, p.osb, p.osh, p.osn), p.osn,
-                       p.lse + seq_stat_off(sp, b, hh, p.H, p.N, p.total), qrow, N, hf, p.vdesc);
+                       p.lse + seq_stat_off(sp, b, hh, p.H, p.N, p.total), qrow, N, hf, p.vdesc,
+                    lds_address(smem) + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * kEpiWaveB<D>, i);
 }
 
 // ----------------------------------------------------------------------------- sparse
@@ -743,6 +767,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
     using C = Cfg<D, F8>;
     using E = typename ElemOf<F8>::type;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
+    static_assert(sizeof(smem) >= (kSpThreads / 64) * kEpiWaveB<D>, "the epilogue stages every wave's rows in LDS");
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, i = lane & 31;
@@ -829,7 +854,8 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_kernel(Params p) {
         kt = ktn;
     }
     epilogue<D, F8>(w, p.o + seq_off(sp, b, hh, p.osb, p.osh, p.osn), p.osn,
-                    p.lse + seq_stat_off(sp, b, hh, p.H, p.N, p.total), qrow, N, hf, p.vdesc);
+                    p.lse + seq_stat_off(sp, b, hh, p.H, p.N, p.total), qrow, N, hf, p.vdesc,
+                    lds_address(smem) + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * kEpiWaveB<D>, i);
 }
 
 // Block-sparse forward, bf16 at head dimension 128, with the K/V tiles loaded straight into
@@ -840,6 +866,7 @@ template <bool CAUSAL>
 __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_dma_kernel(Params p) {
     constexpr int D = 128;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kDmaStageB];
+    static_assert(sizeof(smem) >= (kSpThreads / 64) * kEpiWaveB<D>, "the epilogue stages every wave's rows in LDS");
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, i = lane & 31;
@@ -920,7 +947,8 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_dma_kernel(Params p)
         kt = ktn;
     }
     epilogue<D, false>(w, p.o + seq_off(sp, b, hh, p.osb, p.osh, p.osn), p.osn,
-                       p.lse + seq_stat_off(sp, b, hh, p.H, p.N, p.total), qrow, N, hf, p.vdesc);
+                       p.lse + seq_stat_off(sp, b, hh, p.H, p.N, p.total), qrow, N, hf, p.vdesc,
+                    lds_address(smem) + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * kEpiWaveB<D>, i);
 }
 
 template <int D, bool CAUSAL, bool F8>
