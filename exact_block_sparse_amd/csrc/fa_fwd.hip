@@ -423,7 +423,7 @@ template <int D> constexpr uint32_t kEpiWaveB = 32 * kEpiPitch<D>;
 // instruction would write 64 scattered 8-byte pieces; instead the wave writes its 32 rows
 // into its own LDS area (`lds_wave`: all LDS reads of the loop are done, which the loop's
 // last barrier guarantees) and stores whole rows from there, 16 lanes per row, 16 bytes
-// each. The wave only reads back what it wrote, so no barrier is needed (a wave's LDS
+// each, non-temporal (the kernel never reads O back). The wave only reads back what it wrote, so no barrier is needed (a wave's LDS
 // operations complete in order; the wait below is only for the compiler's benefit).
 template <int D, bool F8>
 __device__ __forceinline__ void epilogue(const Rows<D, F8>& w, uint16_t* obase, int64_t osn, float* lbase, int qrow,
@@ -452,7 +452,7 @@ __device__ __forceinline__ void epilogue(const Rows<D, F8>& w, uint16_t* obase, 
     for (int k = 0; k < 32 / ROWS; ++k) {
         const int r = k * ROWS + lane / CHUNKS;
         const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(lds_wave + r * PITCH + 16 * ch);
-        if (qw0 + r < N) *reinterpret_cast<u32x4*>(obase + (int64_t)(qw0 + r) * osn + 8 * ch) = v;
+        if (qw0 + r < N) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(obase + (int64_t)(qw0 + r) * osn + 8 * ch));
     }
     if (hf == 0 && qrow < N) lbase[qrow] = l_tot > 0.0f ? (w.m_run + log2f(l_tot)) * kLn2 : kNegInf;
 }
