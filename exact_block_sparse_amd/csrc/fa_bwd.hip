@@ -962,20 +962,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(KVParams p) {
         }
     }
 
-    if (key < N) {
-        const float sc_out = pwave ? 1.0f : p.scale;
-        uint16_t* out = pwave ? p.dv + seq_off(sp, b, hk, p.dvsb, p.dvsh, p.dvsn) + (int64_t)key * p.dvsn
-                              : p.dk + seq_off(sp, b, hk, p.dksb, p.dksh, p.dksn) + (int64_t)key * p.dksn;
-#pragma unroll
-        for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                bf16x4 a;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) a[e] = (__bf16)(acc[cb][4 * j + e] * sc_out);
-                *reinterpret_cast<bf16x4*>(out + 32 * cb + 8 * j + 4 * hf) = a;
-            }
-    }
+    // dV (P waves) or dK (dS waves) of the wave's 32 keys, through the LDS the loop has freed
+    static_assert(sizeof(smem) >= 8 * kRowStageWaveB, "every wave stages its rows in LDS");
+    store_rows_staged(acc, pwave ? 1.0f : p.scale, i, hf, lane,
+                      pwave ? p.dv + seq_off(sp, b, hk, p.dvsb, p.dvsh, p.dvsn)
+                            : p.dk + seq_off(sp, b, hk, p.dksb, p.dksh, p.dksn),
+                      pwave ? p.dvsn : p.dksn, k0 + 32 * grp, N, lds0 + (uint32_t)wave_u * kRowStageWaveB);
 }
 
 // ----------------------------------------------------------------------------- dQ
@@ -1367,19 +1359,10 @@ __global__ __launch_bounds__(kThreads, 2) void dq_dma_kernel(QParams p) {
         cur ^= 1;
     }
 
-    if (qrow < N) {
-        uint16_t* dqr = p.dq + seq_off(sp, b, hh, p.dqsb, p.dqsh, p.dqsn) + (int64_t)qrow * p.dqsn;
-        const float sc = p.scale;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                bf16x4 a;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) a[e] = (__bf16)(dq[cb][4 * j + e] * sc);
-                *reinterpret_cast<bf16x4*>(dqr + 32 * cb + 8 * j + 4 * hf) = a;
-            }
-    }
+    // the wave's 32 dQ rows, through the LDS the loop has freed
+    static_assert(sizeof(smem) >= (kThreads / 64) * kRowStageWaveB, "every wave stages its rows in LDS");
+    store_rows_staged(dq, p.scale, i, hf, lane, p.dq + seq_off(sp, b, hh, p.dqsb, p.dqsh, p.dqsn), p.dqsn, qw0, N,
+                      lds_address(smem) + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * kRowStageWaveB);
 }
 
 
@@ -1610,20 +1593,11 @@ __global__ __launch_bounds__(kThreads, 2) void dq_ds_kernel(DsQParams p) {
         cur ^= 1;
     }
 
-    const int qrow = qw0 + swap23(i);
-    if (qrow < N) {
-        uint16_t* dqr = p.dq + seq_off(sp, b, hh, p.dqsb, p.dqsh, p.dqsn) + (int64_t)qrow * p.dqsn;
-        const float sc = p.scale;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                bf16x4 a;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) a[e] = (__bf16)(dq[cb][4 * j + e] * sc);
-                *reinterpret_cast<bf16x4*>(dqr + 32 * cb + 8 * j + 4 * hf) = a;
-            }
-    }
+    // the wave's 32 dQ rows (lane i holds query position i, i.e. row qw0 + swap23(i)), through
+    // the LDS the loop has freed
+    static_assert(sizeof(smem) >= (kThreads / 64) * kRowStageWaveB, "every wave stages its rows in LDS");
+    store_rows_staged(dq, p.scale, swap23(i), hf, lane, p.dq + seq_off(sp, b, hh, p.dqsb, p.dqsh, p.dqsn), p.dqsn, qw0, N,
+                      lds_address(smem) + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * kRowStageWaveB);
 }
 
 template <int D, bool CAUSAL>

@@ -323,4 +323,36 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
     return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
 }
 
+// Output of one wave at head dimension 128: 32 rows held in accumulator order (lane (i, hf),
+// block cb, group j: columns 32 cb + 8 j + 4 hf .. + 3 of local row `lrow`), scaled by `sc`
+// and written as bf16 to rows row0 + r (r < 32, row0 + r < nrows) of a row-major tensor
+// (`base`: row 0, `rs`: row stride in elements, both 16-byte aligned). Stored directly, each
+// store instruction would write 64 scattered 8-byte pieces; staged through the wave's own LDS
+// area (32 rows of kRowStagePitch bytes at `lds_wave`, not in use by any wave when called)
+// whole rows go out, 16 lanes per row, 16 bytes each, non-temporal. The wave reads back only
+// what it wrote, so no barrier is needed.
+constexpr uint32_t kRowStagePitch = 2 * 128 + 16;   // the pad keeps a half's row writes on distinct banks
+constexpr uint32_t kRowStageWaveB = 32 * kRowStagePitch;
+__device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[4], float sc, int lrow, int hf, int lane,
+                                                  uint16_t* base, int64_t rs, int row0, int nrows, uint32_t lds_wave) {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bf16x4 a;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] = (__bf16)(acc[cb][4 * j + e] * sc);
+            *(__attribute__((address_space(3))) bf16x4*)(uintptr_t)(lds_wave + lrow * kRowStagePitch +
+                                                                  2 * (32 * cb + 8 * j + 4 * hf)) = a;
+        }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    const int ch = lane & 15;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int r = 4 * k + (lane >> 4);
+        const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(lds_wave + r * kRowStagePitch + 16 * ch);
+        if (row0 + r < nrows) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base + (int64_t)(row0 + r) * rs + 8 * ch));
+    }
+}
+
 }  // namespace fa
