@@ -389,6 +389,19 @@ __device__ __forceinline__ void pv(const uint16_t* buf, Rows<D, F8>& w, int i, i
     __builtin_amdgcn_sched_group_barrier(0x008, MF - PAIRS, 0);
 }
 
+// Empty running state of a wave's rows: O = 0, no running max, zero row sums.
+template <int D, bool F8>
+__device__ __forceinline__ void init_rows(Rows<D, F8>& w) {
+    using C = Cfg<D, F8>;
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb) w.o[cb] = f32x16{};
+    w.m_run = kNegInf;
+    w.m_neg = 0.0f;
+    w.t_thr = -1.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w.l4[j] = 0.0f;
+}
+
 template <int D, bool F8>
 __device__ __forceinline__ void load_q(Rows<D, F8>& w, const typename ElemOf<F8>::type* qp, int64_t qsn, int qrow,
                                        int N, int hf) {
@@ -404,13 +417,7 @@ __device__ __forceinline__ void load_q(Rows<D, F8>& w, const typename ElemOf<F8>
             w.qf.v[ks] = join8(load16b(a, qrow < N), load16b(a + 16, qrow < N));
         }
     }
-#pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb) w.o[cb] = f32x16{};
-    w.m_run = kNegInf;
-    w.m_neg = 0.0f;
-    w.t_thr = -1.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w.l4[j] = 0.0f;
+    init_rows(w);
 }
 
 // Row pitch of the epilogue's LDS staging area (bytes; the 16-byte pad keeps the row writes
@@ -694,8 +701,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_dma_kernel(Params 
     const int qlast = min(q0 + kPPRows - 1, N - 1);
 
     Rows<D, false> w;
-    load_q<D, false>(w, static_cast<const uint16_t*>(p.q) + seq_off(sp, b, hh, p.qsb, p.qsh, p.qsn), p.qsn, qrow,
-                     N, hf);
+    init_rows(w);
 
     int T = (N + kBK - 1) / kBK;
     if (CAUSAL) T = min(T, qlast / kBK + 1);
@@ -710,12 +716,43 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_dma_kernel(Params 
     // take their LDS address from M0)
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t lds0 = lds_address(smem);
+    // Q: the workgroup's 256 rows go straight into stages 2 and 3 (free until phase 0 loads
+    // step 2), as four 64-row blocks in the K layout, whose row swizzle also serves the
+    // fragment reads below; whole-row loads, like the K/V tiles (each wave fetches the same
+    // two 1-KB pieces of every block as for a K tile).
+    const uint32_t q_lds = lds0 + 2 * kDmaStageB;
+    {
+        const uint16_t* qp = static_cast<const uint16_t*>(p.q) + seq_off(sp, b, hh, p.qsb, p.qsh, p.qsn);
+        uint32_t qoff[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = 4 * (2 * wave + j) + (lane >> 4), slot = lane & 15;
+            qoff[j] = (uint32_t)((int64_t)row * p.qsn * 2 + 16 * (slot ^ swz<kSwzRow>(row)));
+        }
+#pragma unroll
+        for (int blk = 0; blk < kPPRows / 64; ++blk) {
+            const int r0 = q0 + 64 * blk;
+            const i32x4 rq = rsrc_words(qp + (int64_t)r0 * p.qsn, rows_bytes(r0, N, p.qsn, 128, 64));
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                load16_to_lds(rq, qoff[j], q_lds + blk * kLdsTileB + 1024u * (2 * (uint32_t)wave_u + j));
+        }
+    }
+    static_assert(kDmaBufs == 4 && 2 * kDmaStageB == (kPPRows / 64) * kLdsTileB, "Q fills stages 2 and 3");
     if (T > 0) st.issue(kp, vp, p.ksn, p.vsn, 0, N, lds0, wave_u);
     if (T > 1) st.issue(kp, vp, p.ksn, p.vsn, kBK, N, lds0 + kDmaStageB, wave_u);
-    // Settle every outstanding load (Q fragments and the first two steps) before the loop.
+    // Settle every outstanding load (Q and the first two steps) before reading Q.
     __builtin_amdgcn_s_waitcnt(0);
-    const float c = signed_scale(w, p.c);   // after the wait: Q is in registers
     __syncthreads();
+    {
+        // the wave's rows: 32 (wave & 1) + i of 64-row block wave / 2; chunk 2 ks + hf
+        const int r = 32 * (wave & 1) + i;
+        const uint32_t rb = q_lds + (uint32_t)(wave >> 1) * kLdsTileB + (uint32_t)r * 256u;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) w.qf.v[ks] = lds16(rb + 16u * (uint32_t)((2 * ks + hf) ^ swz<kSwzRow>(r)));
+    }
+    const float c = signed_scale(w, p.c);   // Q is in registers
+    __syncthreads();   // every wave has its Q: phase 0 may load step 2 over it
 
     // Phase ph: group g works on local phase lp = ph - g. Even lp = 2t: P.V of step t-1 and
     // S of step t (MFMA); odd lp = 2t+1: softmax of step t (VALU).
