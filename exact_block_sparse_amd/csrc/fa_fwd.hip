@@ -674,6 +674,39 @@ __device__ __forceinline__ void pv_sw(uint32_t so, Rows<128, false>& w, const Dm
     __builtin_amdgcn_sched_group_barrier(0x008, MF - PAIRS, 0);
 }
 
+// Q of a workgroup's ROWS rows (from q0; rows past N read as zeros) straight into LDS at
+// `q_lds`, as ROWS / 64 blocks of 64 rows in the K layout (kSwzRow), with the whole-row loads
+// of the K/V tiles: each of the NW waves fetches the same 1-KB pieces of every block as for a
+// K tile. `q_lds` and `wave_u` must be wave-uniform (the loads take M0).
+template <int NW, int ROWS>
+__device__ __forceinline__ void load_q_to_lds(const uint16_t* qp, int64_t qsn, int q0, int N, uint32_t q_lds,
+                                              int wave, int wave_u, int lane) {
+    constexpr int P = 16 / NW;
+    uint32_t qoff[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        const int row = 4 * (P * wave + j) + (lane >> 4), slot = lane & 15;
+        qoff[j] = (uint32_t)((int64_t)row * qsn * 2 + 16 * (slot ^ swz<kSwzRow>(row)));
+    }
+#pragma unroll
+    for (int blk = 0; blk < ROWS / 64; ++blk) {
+        const int r0 = q0 + 64 * blk;
+        const i32x4 rq = rsrc_words(qp + (int64_t)r0 * qsn, rows_bytes(r0, N, qsn, 128, 64));
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+            load16_to_lds(rq, qoff[j], q_lds + blk * kLdsTileB + 1024u * (P * (uint32_t)wave_u + j));
+    }
+}
+
+// The wave's Q fragments (rows 32 wave + i of the workgroup's rows: row 32 (wave & 1) + i of
+// block wave / 2) from the layout load_q_to_lds writes; the loads must have arrived.
+__device__ __forceinline__ void read_q_frags(Rows<128, false>& w, uint32_t q_lds, int wave, int i, int hf) {
+    const int r = 32 * (wave & 1) + i;
+    const uint32_t rb = q_lds + (uint32_t)(wave >> 1) * kLdsTileB + (uint32_t)r * 256u;
+#pragma unroll
+    for (int ks = 0; ks < 128 / 16; ++ks) w.qf.v[ks] = lds16(rb + 16u * (uint32_t)((2 * ks + hf) ^ swz<kSwzRow>(r)));
+}
+
 template <bool CAUSAL>
 __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_dma_kernel(Params p) {
     constexpr int D = 128;
@@ -717,40 +750,17 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pingpong_dma_kernel(Params 
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t lds0 = lds_address(smem);
     // Q: the workgroup's 256 rows go straight into stages 2 and 3 (free until phase 0 loads
-    // step 2), as four 64-row blocks in the K layout, whose row swizzle also serves the
-    // fragment reads below; whole-row loads, like the K/V tiles (each wave fetches the same
-    // two 1-KB pieces of every block as for a K tile).
+    // step 2), read into the fragments below.
     const uint32_t q_lds = lds0 + 2 * kDmaStageB;
-    {
-        const uint16_t* qp = static_cast<const uint16_t*>(p.q) + seq_off(sp, b, hh, p.qsb, p.qsh, p.qsn);
-        uint32_t qoff[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = 4 * (2 * wave + j) + (lane >> 4), slot = lane & 15;
-            qoff[j] = (uint32_t)((int64_t)row * p.qsn * 2 + 16 * (slot ^ swz<kSwzRow>(row)));
-        }
-#pragma unroll
-        for (int blk = 0; blk < kPPRows / 64; ++blk) {
-            const int r0 = q0 + 64 * blk;
-            const i32x4 rq = rsrc_words(qp + (int64_t)r0 * p.qsn, rows_bytes(r0, N, p.qsn, 128, 64));
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                load16_to_lds(rq, qoff[j], q_lds + blk * kLdsTileB + 1024u * (2 * (uint32_t)wave_u + j));
-        }
-    }
+    load_q_to_lds<kPPThreads / 64, kPPRows>(static_cast<const uint16_t*>(p.q) + seq_off(sp, b, hh, p.qsb, p.qsh, p.qsn),
+                                            p.qsn, q0, N, q_lds, wave, wave_u, lane);
     static_assert(kDmaBufs == 4 && 2 * kDmaStageB == (kPPRows / 64) * kLdsTileB, "Q fills stages 2 and 3");
     if (T > 0) st.issue(kp, vp, p.ksn, p.vsn, 0, N, lds0, wave_u);
     if (T > 1) st.issue(kp, vp, p.ksn, p.vsn, kBK, N, lds0 + kDmaStageB, wave_u);
     // Settle every outstanding load (Q and the first two steps) before reading Q.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    {
-        // the wave's rows: 32 (wave & 1) + i of 64-row block wave / 2; chunk 2 ks + hf
-        const int r = 32 * (wave & 1) + i;
-        const uint32_t rb = q_lds + (uint32_t)(wave >> 1) * kLdsTileB + (uint32_t)r * 256u;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) w.qf.v[ks] = lds16(rb + 16u * (uint32_t)((2 * ks + hf) ^ swz<kSwzRow>(r)));
-    }
+    read_q_frags(w, q_lds, wave, i, hf);
     const float c = signed_scale(w, p.c);   // Q is in registers
     __syncthreads();   // every wave has its Q: phase 0 may load step 2 over it
 
@@ -926,8 +936,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_dma_kernel(Params p)
     const int qlast = min(q0 + kSparseBlock - 1, N - 1);
 
     Rows<D, false> w;
-    load_q<D, false>(w, static_cast<const uint16_t*>(p.q) + seq_off(sp, b, hh, p.qsb, p.qsh, p.qsn), p.qsn, qrow,
-                     N, hf);
+    init_rows(w);
 
     const int nkb = (N + kSparseBlock - 1) / kSparseBlock;
     int64_t lo = load_uniform(p.kv_offsets, qblk), hi = load_uniform(p.kv_offsets, qblk + 1);
@@ -952,10 +961,19 @@ __global__ __launch_bounds__(kSpThreads, 2) void fwd_sparse_dma_kernel(Params p)
     ad.init(i, hf, lds_address(smem));
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t lds0 = lds_address(smem);
+    // Q: the block's 128 rows go straight into stage 1 (free until the first step loads the
+    // next one), read into the fragments below.
+    static_assert(kDmaStageB == (kSparseBlock / 64) * kLdsTileB, "Q fills one stage");
+    const uint32_t q_lds = lds0 + kDmaStageB;
+    load_q_to_lds<kSpThreads / 64, kSparseBlock>(static_cast<const uint16_t*>(p.q) + seq_off(sp, b, hh, p.qsb, p.qsh, p.qsn),
+                                                 p.qsn, q0, N, q_lds, wave, wave_u, lane);
     if (t < t_end) st.issue(kp, vp, p.ksn, p.vsn, kt, N, lds0, wave_u);
+    // Settle every outstanding load (Q and the first step) before reading Q.
     __builtin_amdgcn_s_waitcnt(0);
-    const float c = signed_scale(w, p.c);   // after the wait: Q is in registers
     __syncthreads();
+    read_q_frags(w, q_lds, wave, i, hf);
+    const float c = signed_scale(w, p.c);   // Q is in registers
+    __syncthreads();   // every wave has its Q: the first step may load the next one over it
 
     int cur = 0;
     while (t < t_end) {
