@@ -700,3 +700,45 @@ def test_fp8_forward_seeded_random_mix(fa, seed):
                                         scale=w.scale, sparse=sp)
     assert_close("O", o, O, TOL_OUT)
     assert_close("LSE", lse, L, TOL_LSE)
+
+
+# ----------------------------------------------------------------------------- outputs in padded views
+@pytest.mark.parametrize("sparse", [False, True])
+def test_outputs_into_padded_views_touch_nothing_else(fa, sparse):
+    # The epilogues stage each wave's rows in LDS and store whole rows: with O, dQ, dK, dV
+    # as views into larger buffers (row stride d + 64, eight spare rows per head) the
+    # results must match the oracle and the padding must keep its sentinel.
+    B, H, N, d = 1, 2, 333, 128
+    w = W.small(B, H, N, d, causal=True, seed=91, direction="bwd", sigma=0.5)
+    x = W.make_inputs(w)
+    q, k, v, do = (x[n].to("cuda") for n in ("q", "k", "v", "do"))
+    sentinel = 7.0
+
+    def padded():
+        buf = torch.full((B, H, N + 8, d + 64), sentinel, dtype=torch.bfloat16, device="cuda")
+        return buf, buf[:, :, :N, :d]
+
+    def untouched(buf):
+        return bool((buf[:, :, N:, :] == sentinel).all()) and bool((buf[:, :, :, d:] == sentinel).all())
+
+    ob, o = padded()
+    if sparse:
+        off, idx = fa.make_block_lists(3, 1, 2, causal=True, rule="strided")
+        o, lse = fa.attn_fwd(q, k, v, causal=True, scale=w.scale, kv_offsets=off, kv_indices=idx, out=o)
+        sp = dict(block=128, window=1, stride=2, rule="strided")
+    else:
+        o, lse = fa.fwd(q, k, v, causal=True, scale=w.scale, out=o)
+        sp = None
+    (dqb, dq), (dkb, dk), (dvb, dv) = padded(), padded(), padded()
+    kw = dict(kv_offsets=off, kv_indices=idx) if sparse else {}
+    fa.attn_bwd_noalloc(q, k, v, o, lse, do, causal=True, scale=w.scale, dq=dq, dk=dk, dv=dv, **kw)
+    torch.cuda.synchronize()
+    for name, buf in (("O", ob), ("dQ", dqb), ("dK", dkb), ("dV", dvb)):
+        assert untouched(buf), f"{name}: padding overwritten"
+    dQ, dK, dV, O, L = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], causal=True, scale=w.scale,
+                                                 sparse=sp, return_forward=True)
+    assert_close("O", o, O, TOL_OUT)
+    assert_close("LSE", lse, L, TOL_LSE)
+    assert_close("dQ", dq, dQ, TOL_OUT)
+    assert_close("dK", dk, dK, TOL_OUT)
+    assert_close("dV", dv, dV, TOL_OUT)
