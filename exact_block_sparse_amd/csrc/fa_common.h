@@ -331,7 +331,7 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 // area (32 rows of kRowStagePitch bytes at `lds_wave`, not in use by any wave when called)
 // whole rows go out, 16 lanes per row, 16 bytes each, non-temporal. The wave reads back only
 // what it wrote, so no barrier is needed.
-constexpr uint32_t kRowStagePitch = 2 * 128 + 16;   // the pad keeps a half's row writes on distinct banks
+constexpr uint32_t kRowStagePitch = 2 * 128 + 16;   // the pad spreads a wave's row writes evenly over the banks
 constexpr uint32_t kRowStageWaveB = 32 * kRowStagePitch;
 __device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[4], float sc, int lrow, int hf, int lane,
                                                   uint16_t* base, int64_t rs, int row0, int nrows, uint32_t lds_wave) {
