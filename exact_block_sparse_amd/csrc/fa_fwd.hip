@@ -420,8 +420,8 @@ __device__ __forceinline__ void load_q(Rows<D, F8>& w, const typename ElemOf<F8>
     init_rows(w);
 }
 
-// Row pitch of the epilogue's LDS staging area (bytes; the 16-byte pad keeps the row writes
-// of the 32 lanes of a half on distinct banks) and the area of one wave (its 32 rows).
+// Row pitch of the epilogue's LDS staging area (bytes; the 16-byte pad spreads the row writes
+// of a wave evenly over the banks) and the area of one wave (its 32 rows).
 template <int D> constexpr uint32_t kEpiPitch = 2 * D + 16;
 template <int D> constexpr uint32_t kEpiWaveB = 32 * kEpiPitch<D>;
 
