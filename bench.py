@@ -64,6 +64,65 @@ def measured_traffic():
     return int(d["traffic_bytes"]) if d else None
 
 
+class LiveClock:
+    """Shader clock and socket power read from the GPU's metrics table (amdsmi: the mean of the
+    8 XCDs' current GFX clocks, MHz; socket power, W) every 20 ms on a host thread. The table
+    trails the load by a fraction of a second, so the readings are taken over a window of
+    back-to-back headline calls right after the timed ones, and the window's first second is
+    left out. Reading the table touches no GPU work; where amdsmi is missing or refuses, the
+    figures are None."""
+
+    def __init__(self):
+        self.samples, self._stop, self._th, self._h = [], None, None, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception:
+            self._h = None
+
+    def _loop(self):
+        import time
+        while not self._stop.is_set():
+            try:
+                m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+                clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
+                if not clks and isinstance(m.get("current_gfxclk"), (int, float)):
+                    clks = [m["current_gfxclk"]]
+                pw = m.get("current_socket_power")
+                if clks:
+                    self.samples.append((time.perf_counter(), sum(clks) / len(clks),
+                                         pw if isinstance(pw, (int, float)) else None))
+            except Exception:
+                return
+            time.sleep(0.02)
+
+    def __enter__(self):
+        import threading
+        import time
+        self.t0 = time.perf_counter()
+        if self._h is not None:
+            self._stop = threading.Event()
+            self._th = threading.Thread(target=self._loop, daemon=True)
+            self._th.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._th is not None:
+            self._stop.set()
+            self._th.join()
+        return False
+
+    def summary(self, skip_s: float = 1.0):
+        kept = [(c, w) for ts, c, w in self.samples if ts >= self.t0 + skip_s]
+        if not kept:
+            return None, None
+        ghz = sum(c for c, _ in kept) / len(kept) / 1e3
+        pws = [w for _, w in kept if w is not None]
+        return round(ghz, 4), (round(sum(pws) / len(pws), 1) if pws else None)
+
+
 def measured_clock_ghz():
     """Shader clock of the headline kernel under load: GRBM_GUI_ACTIVE cycles (summed over
     the 8 XCDs, so divided by 8) per second of dispatch, from the committed counter run."""
@@ -372,6 +431,14 @@ def main():
     head = prepare(fa, W, torch, HEADLINE)
     log(f"[bench] timing {HEADLINE}: warmup {args.warmup}, steps {args.steps}")
     t = timer.run(head["fn"], args.steps, args.warmup)
+    live = LiveClock()
+    with live:   # about 2.5 s of back-to-back headline calls, not timed
+        end = time.perf_counter() + 2.5
+        while time.perf_counter() < end:
+            for _ in range(10):
+                head["fn"]()
+            torch.cuda.synchronize()
+    live_ghz, live_w = live.summary()
     hs = summarize(head, t)
     log(f"[bench] {HEADLINE}: {hs['ms_mean']} ms, {hs['tflops']} TFLOP/s ({hs['pct_peak']}% of peak)")
     w = head["workload"]
@@ -438,7 +505,12 @@ def main():
                      # this kernel's load (GRBM_GUI_ACTIVE, committed counter run), not 2.4 GHz
                      "clock_ghz_measured": clock,
                      "pct_of_measured_clock_peak": (round(100 * achieved / (N_CU * BF16_FLOP_PER_CU_CLK * clock / 1e3),
-                                                          2) if clock else None)},
+                                                          2) if clock else None),
+                     # the clock and socket power read live during this run's timed headline calls
+                     "clock_ghz_live": live_ghz,
+                     "pct_of_live_clock_peak": (round(100 * achieved / (N_CU * BF16_FLOP_PER_CU_CLK * live_ghz / 1e3), 2)
+                                                if live_ghz else None),
+                     "socket_power_w_live": live_w},
         "cpu_baseline": cpu,
         "workloads": others,
         "bwd_schedule": args.bwd_schedule,
